@@ -1,0 +1,253 @@
+#!/usr/bin/env python3
+"""Benchmark of MLA tree-verify attention on one MI355X.
+
+Headline workload (one step = one call = split-KV kernel + combine kernel):
+  binary16-ctx65536: batch 1, 16-node heap-binary tree, 8 heads, context 65536,
+  pool of 262144 slots, fully scattered page_size=1 table, bf16 latents ~ N(0,1),
+  scale 1/sqrt(192). Eight independently seeded input sets (pool, Q) rotate from
+  call to call so that the 256 MB Infinity Cache cannot serve a repeat.
+Metric: achieved GB/s = algorithmic bytes per call / time per call, where the
+algorithmic bytes are every referenced 1152-byte row and its 4-byte index once,
+Q, out, lse and the mask.
+
+Also reported on the same line:
+  roofline     the split-KV kernel's algorithmic bytes / its average launch
+               duration (HIP events around each launch), against 8 TB/s;
+  context_sweep the 61-layer stacked chain8 sweep (own pool per layer, one page
+               table per context): microseconds per layer and GB/s;
+  cpu_baseline the CPU oracle on one full call of the headline workload.
+
+Prints progress to stderr and one JSON line to stdout.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "achieved HBM GB/s (% of peak) for MLA tree-verify at 64k/185k ctx; µs/layer"
+PEAK_GBPS = 8000.0
+LAYERS = 61
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def split_kernel_bytes(seq_lens, n, h):
+    """Algorithmic bytes the split-KV kernel must read: rows, indices, Q, mask."""
+    from mla_tree_verify_02_amd import inputs as I
+    w = I.mask_words(n)
+    return sum(int(s) for s in seq_lens) * (I.ROW_BYTES + 4) + len(seq_lens) * (
+        n * h * I.D_QK * 2 + n * w * 4)
+
+
+def time_calls(calls, steps, warmup, torch):
+    """Wall-clock of `steps` calls (rotating), synchronised on both sides."""
+    for k in range(warmup):
+        calls[k % len(calls)].run()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(steps):
+        calls[k % len(calls)].run()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) / steps
+
+
+def time_split_kernel(calls, steps, torch):
+    """Average split-KV kernel duration from HIP events around each launch on
+    the stream the library launches on (torch's current stream)."""
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    torch.cuda.synchronize()
+    for k in range(steps):
+        ev[k][0].record(stream)
+        calls[k % len(calls)].splitkv()
+        ev[k][1].record(stream)
+    torch.cuda.synchronize()
+    ms = [a.elapsed_time(b) for a, b in ev]
+    ms.sort()
+    return sum(ms) / len(ms), ms[len(ms) // 2]
+
+
+def headline(args, torch, M, I):
+    log("building headline inputs (binary16-ctx65536, %d rotated sets)" % args.rotate)
+    wls = [I.config_workload(2, device="cuda", layer=r) for r in range(args.rotate)]
+    ws = None
+    calls = []
+    for wl in wls:
+        c = M.prepare_workload(wl, workspace=ws)
+        ws = c.workspace
+        calls.append(c)
+    seq = wls[0].seq_lens_host()
+    n, h = wls[0].num_nodes, wls[0].num_heads
+    call_bytes = I.algorithmic_bytes(seq, n, h)
+    log("timing %d steps after %d warmup" % (args.steps, args.warmup))
+    sec = time_calls(calls, args.steps, args.warmup, torch)
+    log("split-KV kernel events over %d launches" % args.steps)
+    avg_ms, med_ms = time_split_kernel(calls, args.steps, torch)
+    kbytes = split_kernel_bytes(seq, n, h)
+    plan = M.plan_query(M.make_shape(1, n, h, wls[0].max_kv, wls[0].num_slots),
+                        torch.cuda.get_device_properties(0).multi_processor_count)
+    return dict(wls=wls, sec=sec, call_bytes=call_bytes, split_avg_ms=avg_ms,
+                split_med_ms=med_ms, split_bytes=kbytes, plan=plan)
+
+
+def sweep(args, torch, M, I):
+    ctxs = [int(c) for c in args.sweep.split(",") if c.strip()]
+    if not ctxs:
+        return []
+    P = 262144
+    log("building %d layer pools of %d slots for the sweep" % (LAYERS, P))
+    pools = [I._randn_bf16((P, I.D_QK), I._gen(I.seed_for(3, l, I.F_KV), "cuda"), "cuda")
+             for l in range(LAYERS)]
+    qs = [I._randn_bf16((64, I.D_QK), I._gen(I.seed_for(3, l, I.F_Q), "cuda"), "cuda").view(1, 8, 8, I.D_QK)
+          for l in range(LAYERS)]
+    mask = torch.from_numpy(I.ancestor_bitmask(I.chain_parents(8)).view("int32").copy()).view(1, 8, 1).cuda()
+    results = []
+    ws = None
+    for ctx in ctxs:
+        S = ctx + 8
+        rows, _ = I.scattered_table([S], P, I.seed_for(3, 0, I.F_TABLE) + ctx)
+        table = torch.from_numpy(rows[0].reshape(1, S).copy()).cuda()
+        seq = torch.tensor([S], dtype=torch.int32, device="cuda")
+        calls = []
+        for l in range(LAYERS):
+            c = M.PreparedCall(qs[l], pools[l], table, seq, mask, I.DEFAULT_SCALE, workspace=ws)
+            ws = c.workspace
+            calls.append(c)
+        steps = max(2, args.sweep_steps)
+        for c in calls:  # warm-up step
+            c.run()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            for c in calls:
+                c.run()
+        torch.cuda.synchronize()
+        step_s = (time.perf_counter() - t0) / steps
+        us_layer = step_s / LAYERS * 1e6
+        b_layer = I.algorithmic_bytes([S], 8, 8)
+        gbps = b_layer / (us_layer * 1e-6) / 1e9
+        results.append({"context": ctx, "layers": LAYERS, "us_per_layer": round(us_layer, 3),
+                        "ms_per_step": round(step_s * 1e3, 4), "gbps": round(gbps, 1),
+                        "pct_of_peak": round(100 * gbps / PEAK_GBPS, 2),
+                        "bytes_per_step": LAYERS * b_layer,
+                        "tokens_per_s_equiv": round(1.0 / step_s, 2)})
+        log("sweep ctx %d: %.2f us/layer, %.0f GB/s" % (ctx, us_layer, gbps))
+        del calls
+    return results
+
+
+def cpu_baseline(wl, call_bytes, I):
+    from oracle import oracle as O
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count() or 1
+    threads = max(1, min(16, cores))
+    log("CPU oracle on one full call with %d threads" % threads)
+    host = (wl.np_q(), wl.np_kv(), wl.np_page_table(), wl.np_seq_lens(), wl.np_mask())
+    t0 = time.perf_counter()
+    O.run(*host, wl.scale, threads=threads)
+    dt = time.perf_counter() - t0
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"value": round(call_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": threads,
+            "kind": "oracle", "seconds": round(dt, 3), "cpu_model": model,
+            "sample": "one full call (all %d rows) of the binary16-ctx65536 workload, input set 0"
+                      % (wl.batch * wl.num_nodes * wl.num_heads)}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--rotate", type=int, default=8, help="independent input sets cycled over")
+    ap.add_argument("--sweep", default="65536,189440",
+                    help="contexts of the 61-layer chain8 sweep ('' to skip)")
+    ap.add_argument("--sweep-steps", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: the verify attention here runs on a single device "
+              "and there is no multi-GPU path to time (requested --gpus %d, WORLD_SIZE %d)"
+              % (args.gpus, world), file=sys.stderr)
+        return 2
+
+    import torch
+
+    import mla_tree_verify_02_amd as M
+    from mla_tree_verify_02_amd import inputs as I
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    M.load()
+    props = torch.cuda.get_device_properties(0)
+    log("device %s, %d CUs" % (props.name, props.multi_processor_count))
+
+    hd = headline(args, torch, M, I)
+    sec = hd["sec"]
+    value = hd["call_bytes"] / sec / 1e9
+    achieved = hd["split_bytes"] / (hd["split_avg_ms"] * 1e-3) / 1e9
+    log("headline: %.2f us/call, %.0f GB/s; split kernel %.2f us avg (%.2f med), %.0f GB/s"
+        % (sec * 1e6, value, hd["split_avg_ms"] * 1e3, hd["split_med_ms"] * 1e3, achieved))
+
+    sw = sweep(args, torch, M, I)
+    cpu = None if args.no_cpu_baseline else cpu_baseline(hd["wls"][0], hd["call_bytes"], I)
+
+    wl = hd["wls"][0]
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(sec * 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic: seeded N(0,1) bf16 latents and queries, scattered page_size=1 table, "
+                "%d rotated input sets" % args.rotate,
+        "config": {"workload": "binary16-ctx65536", "batch": 1, "num_nodes": wl.num_nodes,
+                   "num_heads": wl.num_heads, "context": wl.prefix_lens[0],
+                   "num_slots": wl.num_slots, "tree": "heap-binary depth 4",
+                   "layout": "scattered page_size=1", "rotated_input_sets": args.rotate,
+                   "plan": hd["plan"]},
+        "us_per_layer": round(sec * 1e6, 3),
+        "pct_of_peak": round(100 * value / PEAK_GBPS, 2),
+        "roofline": {"bound": "hbm", "kernel": "split_kernel",
+                     "achieved": round(achieved, 1), "peak": PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_GBPS, 4), "traffic": None,
+                     "avg_launch_us": round(hd["split_avg_ms"] * 1e3, 3),
+                     "bytes_per_launch": hd["split_bytes"]},
+        "context_sweep": sw,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

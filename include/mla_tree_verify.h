@@ -1,0 +1,180 @@
+/*
+ * mla_tree_verify.h -- C ABI of the MI355X (gfx950) absorbed-MLA tree-verify
+ * attention library (libmla_tree_verify.so).
+ *
+ * The operation. In the speculative tree-verify decode step, every node of a
+ * small draft tree (about nine of them, "The Moment of Certainty", section
+ * Message 12190) queries, for each head, a long compressed-latent KV cache kept
+ * in a pool with one token per page and reached through a per-token page table
+ * ("The 130x Slowdown", The Reasoning, step 4; "The Moment of Certainty", The
+ * User Provides the Final Piece, for why the page size is 1). The long prefix is
+ * visible to every node; the tree block that follows it is filtered by a
+ * per-node visibility bitmask ("The Moment of Certainty", The Path Forward;
+ * "The GPU That Wasn't There", The Native Engine Thesis). In absorbed form the
+ * 576-wide latent row is the key and its first 512 elements are the value
+ * ("The 130x Slowdown", The Technical Depth). For sequence b, node i, head h:
+ *
+ *   V(b,i)  = { p < S_b - N }  u  { S_b - N + j : bit j of tree_mask[b][i] }
+ *   s_p     = scale * < q[b][i][h][0:576], kv_pool[page_table[b][p]][0:576] >
+ *   lse     = ln sum_{p in V} exp(s_p)                          (natural log)
+ *   out     = sum_{p in V} exp(s_p - lse) * kv_pool[page_table[b][p]][0:512]
+ *
+ * An empty visible set yields out = 0 and lse = -inf.
+ *
+ * How it runs: a split-KV kernel (each workgroup takes one slice of one
+ * sequence's key positions for up to 64 query rows, stages the slice's page
+ * indices and the gathered 1152-byte rows in LDS, and runs Q.K^T and P.V on
+ * bf16 MFMA with an online softmax in fp32), then a log-sum-exp combine kernel
+ * that merges the slices and writes out and lse. Both are enqueued on `stream`.
+ */
+#ifndef MLA_TREE_VERIFY_H
+#define MLA_TREE_VERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ------------------------------------------------------------------ limits */
+#define MTV_D_LATENT 512      /* value / latent width                        */
+#define MTV_D_ROPE 64         /* RoPE key width                              */
+#define MTV_D_QK 576          /* key and absorbed-query width (512 + 64)     */
+#define MTV_MAX_NODES 64      /* tree nodes per sequence (two mask words)    */
+#define MTV_MAX_BATCH 65535
+#define MTV_MAX_KV (1 << 26)  /* key positions per sequence                  */
+
+/* ------------------------------------------------------------ status codes */
+#define MTV_OK 0
+#define MTV_ERR_NULL -1       /* a required pointer is NULL                  */
+#define MTV_ERR_SHAPE -2      /* shape outside the limits above              */
+#define MTV_ERR_ALIGN -3      /* q, kv_pool or out not 16-byte aligned, or a
+                                 4-byte array or the workspace misaligned     */
+#define MTV_ERR_WORKSPACE -4  /* workspace_bytes below the required size     */
+#define MTV_ERR_HIP -5        /* the HIP runtime refused a query or a launch */
+
+/*
+ * Problem shape. All fields are host values.
+ *   batch      B >= 1 sequences
+ *   num_nodes  N in [1, 64] tree nodes per sequence
+ *   num_heads  H >= 1 query heads (N * H <= 65536 query rows per sequence)
+ *   max_kv     row length of page_table; every S_b must lie in [N, max_kv]
+ *   num_slots  rows in kv_pool, in [1, 2^31)
+ */
+typedef struct {
+    int32_t batch;
+    int32_t num_nodes;
+    int32_t num_heads;
+    int32_t max_kv;
+    int64_t num_slots;
+} mtv_shape;
+
+/*
+ * Bytes of device workspace mla_tree_verify needs for `shape` on the current
+ * device (the split plan depends on the device's compute-unit count). Returns 0
+ * if the shape is invalid. Host-only; never synchronises.
+ */
+size_t mla_tree_verify_workspace_size(const mtv_shape* shape);
+
+/*
+ * Enqueue the verify attention on `stream` (NULL: the null stream).
+ *
+ * Device pointers (all caller-owned; the library never allocates, frees or
+ * synchronises, so the call may be captured into a HIP graph):
+ *   q          bf16 [B][N][H][576]  absorbed query, q_latent[512] | q_rope[64]
+ *                                   (RoPE already applied); 16-byte aligned
+ *   kv_pool    bf16 [num_slots][576] latent[512] | rope_k[64], 1152 B per row;
+ *                                   16-byte aligned
+ *   page_table int32 [B][max_kv]    pool slot of key position p of sequence b.
+ *                                   Positions [0, S_b - N) are the prefix;
+ *                                   positions [S_b - N, S_b) are tree nodes
+ *                                   0..N-1 in node order. Entries at p >= S_b
+ *                                   are never used.
+ *   seq_lens   int32 [B]            S_b = prefix length + N
+ *   tree_mask  uint32 [B][N][W], W = ceil(N/32): node i may attend tree node j
+ *                                   iff bit (j & 31) of word (j >> 5) is set.
+ *                                   Bits for j >= N are ignored.
+ *   scale      softmax scale applied to the full 576-wide dot (e.g. 1/sqrt(192))
+ *   out        bf16 [B][N][H][512]  written in full (round to nearest even)
+ *   lse        fp32 [B][N][H]       natural-log sum of exp(scaled scores)
+ *   workspace  >= mla_tree_verify_workspace_size(shape) bytes, 256-byte aligned;
+ *              scratch for per-slice partial results. Its contents need no
+ *              initialisation and are meaningless after the call.
+ *
+ * Outputs must not alias inputs or the workspace. Calls that share a workspace
+ * must be ordered on one stream.
+ *
+ * Errors: returns MTV_OK or a negative MTV_ERR_* code. Only host-visible
+ * arguments are validated (no device memory is read on the host). Device
+ * contents are clamped inside the kernels so that no access leaves its buffer:
+ * S_b is clamped to [N, max_kv] and page indices to [0, num_slots); such
+ * out-of-range values give unspecified results but never a fault. Rows
+ * referenced at positions < S_b should hold finite values: a non-finite tree
+ * row can reach nodes that mask it out (it is multiplied by a zero weight).
+ */
+int mla_tree_verify(const mtv_shape* shape,
+                    const void* q,
+                    const void* kv_pool,
+                    const int32_t* page_table,
+                    const int32_t* seq_lens,
+                    const uint32_t* tree_mask,
+                    float scale,
+                    void* out,
+                    float* lse,
+                    void* workspace,
+                    size_t workspace_bytes,
+                    hipStream_t stream);
+
+/*
+ * The two phases of mla_tree_verify, for callers that time them apart or that
+ * merge slice partials themselves (for instance slices computed on several
+ * devices, each holding part of a sequence's key positions).
+ *
+ * mla_tree_verify_splitkv enqueues only the split-KV kernel: it takes the same
+ * inputs as mla_tree_verify and leaves, in `workspace`, one partial per
+ * (sequence, 64-row group, key slice): the unnormalised weighted latent sum,
+ * the running max of the scaled scores in log2 units and the sum of
+ * 2^(score*log2(e) - max). mla_tree_verify_combine merges those partials by
+ * log-sum-exp and writes out and lse. The combine must run on a workspace
+ * filled by a splitkv call with the same shape on the same device (the layout
+ * follows mtv_plan_query), ordered after it on a stream. Arguments, alignment
+ * and error codes are those of mla_tree_verify; mla_tree_verify is exactly
+ * the splitkv call followed by the combine call on the same stream.
+ */
+int mla_tree_verify_splitkv(const mtv_shape* shape,
+                            const void* q,
+                            const void* kv_pool,
+                            const int32_t* page_table,
+                            const int32_t* seq_lens,
+                            const uint32_t* tree_mask,
+                            float scale,
+                            void* workspace,
+                            size_t workspace_bytes,
+                            hipStream_t stream);
+
+int mla_tree_verify_combine(const mtv_shape* shape,
+                            const int32_t* seq_lens,
+                            void* out,
+                            float* lse,
+                            void* workspace,
+                            size_t workspace_bytes,
+                            hipStream_t stream);
+
+/* Static, human-readable text for a status code. */
+const char* mtv_status_string(int status);
+
+/*
+ * Introspection of the split plan the library uses for `shape` on a device with
+ * `num_cus` compute units: key slices per sequence (*splits), keys per slice
+ * (*chunk, a multiple of 32) and 64-row groups per sequence (*row_groups).
+ * Host-only arithmetic. Returns MTV_OK, MTV_ERR_NULL or MTV_ERR_SHAPE.
+ */
+int mtv_plan_query(const mtv_shape* shape, int num_cus, int* splits, int* chunk, int* row_groups);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MLA_TREE_VERIFY_H */

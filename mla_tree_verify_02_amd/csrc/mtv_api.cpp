@@ -1,0 +1,217 @@
+// Host side of the C ABI: argument validation, the split plan, workspace
+// layout and the two launches. Never allocates, frees or synchronises.
+#include <atomic>
+#include <cmath>
+#include <cstdint>
+
+#include "mla_tree_verify.h"
+#include "mtv_internal.h"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_cu_count[kMaxDevices];  // zero-initialised: unknown
+
+// Compute units of the current device, cached per device id.
+int current_cu_count()
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+        return -1;
+    int c = g_cu_count[dev].load(std::memory_order_relaxed);
+    if (c > 0)
+        return c;
+    if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || c <= 0)
+        return -1;
+    g_cu_count[dev].store(c, std::memory_order_relaxed);
+    return c;
+}
+
+bool shape_ok(const mtv_shape& s)
+{
+    if (s.batch < 1 || s.batch > MTV_MAX_BATCH)
+        return false;
+    if (s.num_nodes < 1 || s.num_nodes > MTV_MAX_NODES)
+        return false;
+    if (s.num_heads < 1 || (int64_t)s.num_nodes * s.num_heads > 65536)
+        return false;
+    if (s.max_kv < s.num_nodes || s.max_kv > MTV_MAX_KV)
+        return false;
+    if (s.num_slots < 1 || s.num_slots > INT32_MAX)
+        return false;
+    return true;
+}
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// The plan: enough slices per sequence that the batch's (sequence, row group)
+// pairs give about one workgroup per compute unit, each slice a whole number of
+// 32-key tiles and at most kMaxChunk keys.
+mtv::Plan make_plan(const mtv_shape& s, int cus)
+{
+    mtv::Plan p{};
+    p.rows = s.num_nodes * s.num_heads;
+    p.row_groups = (p.rows + mtv::kRowsPerGroup - 1) / mtv::kRowsPerGroup;
+    const int64_t tiles = (s.max_kv + mtv::kTileKeys - 1) / mtv::kTileKeys;
+    const int64_t pairs = (int64_t)s.batch * p.row_groups;
+    int64_t splits = (cus + pairs - 1) / pairs;
+    if (splits < 1)
+        splits = 1;
+    if (splits > tiles)
+        splits = tiles;
+    int64_t chunk_tiles = (tiles + splits - 1) / splits;
+    const int64_t max_tiles = mtv::kMaxChunk / mtv::kTileKeys;
+    if (chunk_tiles > max_tiles)
+        chunk_tiles = max_tiles;
+    splits = (tiles + chunk_tiles - 1) / chunk_tiles;
+    p.splits = (int)splits;
+    p.chunk = (int)(chunk_tiles * mtv::kTileKeys);
+    const size_t parts = (size_t)pairs * (size_t)p.splits;
+    p.part_o_off = 0;
+    p.part_ml_off = align_up(parts * mtv::kRowsPerGroup * mtv::kDv * sizeof(float), 256);
+    p.bytes = align_up(p.part_ml_off + parts * mtv::kRowsPerGroup * 2 * sizeof(float), 256);
+    return p;
+}
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+size_t mla_tree_verify_workspace_size(const mtv_shape* shape)
+{
+    if (!shape || !shape_ok(*shape))
+        return 0;
+    int cus = current_cu_count();
+    if (cus <= 0)
+        cus = 256;  // no device visible: size for a full MI355X
+    return make_plan(*shape, cus).bytes;
+}
+
+int mtv_plan_query(const mtv_shape* shape, int num_cus, int* splits, int* chunk, int* row_groups)
+{
+    if (!shape || !splits || !chunk || !row_groups)
+        return MTV_ERR_NULL;
+    if (!shape_ok(*shape) || num_cus < 1)
+        return MTV_ERR_SHAPE;
+    const mtv::Plan p = make_plan(*shape, num_cus);
+    *splits = p.splits;
+    *chunk = p.chunk;
+    *row_groups = p.row_groups;
+    return MTV_OK;
+}
+
+}  // extern "C"
+
+namespace {
+
+enum Phase { kSplit = 1, kCombine = 2 };
+
+// Shared validation and dispatch of the three launching entry points. Pointers
+// a phase does not use may be NULL for that phase.
+int run(int phases, const mtv_shape* shape, const void* q, const void* kv_pool,
+        const int32_t* page_table, const int32_t* seq_lens, const uint32_t* tree_mask,
+        float scale, void* out, float* lse, void* workspace, size_t workspace_bytes,
+        hipStream_t stream)
+{
+    const bool split = phases & kSplit;
+    const bool combine = phases & kCombine;
+    if (!shape || !seq_lens || !workspace)
+        return MTV_ERR_NULL;
+    if (split && (!q || !kv_pool || !page_table || !tree_mask))
+        return MTV_ERR_NULL;
+    if (combine && (!out || !lse))
+        return MTV_ERR_NULL;
+    if (!shape_ok(*shape) || (split && !std::isfinite(scale)))
+        return MTV_ERR_SHAPE;
+    if (!aligned(seq_lens, 4) || !aligned(workspace, 256))
+        return MTV_ERR_ALIGN;
+    if (split && (!aligned(q, 16) || !aligned(kv_pool, 16) || !aligned(page_table, 4) ||
+                  !aligned(tree_mask, 4)))
+        return MTV_ERR_ALIGN;
+    if (combine && (!aligned(out, 16) || !aligned(lse, 4)))
+        return MTV_ERR_ALIGN;
+    const int cus = current_cu_count();
+    if (cus <= 0)
+        return MTV_ERR_HIP;
+    const mtv::Plan plan = make_plan(*shape, cus);
+    if (workspace_bytes < plan.bytes)
+        return MTV_ERR_WORKSPACE;
+
+    mtv::Args a{};
+    a.q = q;
+    a.kv = kv_pool;
+    a.page_table = page_table;
+    a.seq_lens = seq_lens;
+    a.tree_mask = tree_mask;
+    a.scale = scale;
+    a.out = out;
+    a.lse = lse;
+    a.part_o = (float*)((char*)workspace + plan.part_o_off);
+    a.part_ml = (float*)((char*)workspace + plan.part_ml_off);
+    a.batch = shape->batch;
+    a.nodes = shape->num_nodes;
+    a.heads = shape->num_heads;
+    a.max_kv = shape->max_kv;
+    a.num_slots = shape->num_slots;
+    if (split && mtv::launch_split(plan, a, stream) != hipSuccess)
+        return MTV_ERR_HIP;
+    if (combine && mtv::launch_combine(plan, a, stream) != hipSuccess)
+        return MTV_ERR_HIP;
+    return MTV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int mla_tree_verify(const mtv_shape* shape, const void* q, const void* kv_pool,
+                    const int32_t* page_table, const int32_t* seq_lens, const uint32_t* tree_mask,
+                    float scale, void* out, float* lse, void* workspace, size_t workspace_bytes,
+                    hipStream_t stream)
+{
+    // every pointer is required here, including those of the combine phase
+    if (!out || !lse || !q || !kv_pool || !page_table || !tree_mask)
+        return MTV_ERR_NULL;
+    return run(kSplit | kCombine, shape, q, kv_pool, page_table, seq_lens, tree_mask, scale, out,
+               lse, workspace, workspace_bytes, stream);
+}
+
+int mla_tree_verify_splitkv(const mtv_shape* shape, const void* q, const void* kv_pool,
+                            const int32_t* page_table, const int32_t* seq_lens,
+                            const uint32_t* tree_mask, float scale, void* workspace,
+                            size_t workspace_bytes, hipStream_t stream)
+{
+    return run(kSplit, shape, q, kv_pool, page_table, seq_lens, tree_mask, scale, nullptr, nullptr,
+               workspace, workspace_bytes, stream);
+}
+
+int mla_tree_verify_combine(const mtv_shape* shape, const int32_t* seq_lens, void* out, float* lse,
+                            void* workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    return run(kCombine, shape, nullptr, nullptr, nullptr, seq_lens, nullptr, 0.f, out, lse,
+               workspace, workspace_bytes, stream);
+}
+
+const char* mtv_status_string(int status)
+{
+    switch (status) {
+    case MTV_OK:
+        return "success";
+    case MTV_ERR_NULL:
+        return "a required pointer is NULL";
+    case MTV_ERR_SHAPE:
+        return "shape or scalar argument out of range";
+    case MTV_ERR_ALIGN:
+        return "misaligned pointer (q, kv_pool, out need 16 B; workspace 256 B; arrays 4 B)";
+    case MTV_ERR_WORKSPACE:
+        return "workspace smaller than mla_tree_verify_workspace_size()";
+    case MTV_ERR_HIP:
+        return "HIP runtime error (no device, or a launch failed)";
+    default:
+        return "unknown status";
+    }
+}
+
+}  // extern "C"

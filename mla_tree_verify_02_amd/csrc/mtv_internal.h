@@ -1,0 +1,46 @@
+// Internal interface between the host API (mtv_api.cpp) and the kernels
+// (mtv_kernels.hip). Not installed; not part of the C ABI.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+namespace mtv {
+
+constexpr int kDqk = 576;          // key / absorbed query width
+constexpr int kDv = 512;           // value width (the latent)
+constexpr int kRowBytes = kDqk * 2;
+constexpr int kTileKeys = 32;      // keys per LDS tile
+constexpr int kRowsPerGroup = 64;  // query rows per split workgroup (4 waves x 16)
+constexpr int kMaxChunk = 8192;    // keys per split (bounded by LDS index staging)
+
+// How one call is cut into workgroups. Depends only on host values.
+struct Plan {
+    int rows;          // R = N * H query rows per sequence
+    int row_groups;    // ceil(R / 64)
+    int splits;        // key slices per sequence
+    int chunk;         // keys per slice, a multiple of kTileKeys
+    size_t part_o_off, part_ml_off, bytes;  // workspace layout
+};
+
+struct Args {
+    const void* q;
+    const void* kv;
+    const int32_t* page_table;
+    const int32_t* seq_lens;
+    const uint32_t* tree_mask;
+    float scale;
+    void* out;
+    float* lse;
+    float* part_o;   // [B][G][splits][64 rows as 4 waves x 32 col-blocks x 64 lanes x 4]
+    float* part_ml;  // [B][G][splits][64 rows][2]  (running max in log2 units, sum)
+    int batch, nodes, heads, max_kv;
+    int64_t num_slots;
+};
+
+hipError_t launch_split(const Plan& plan, const Args& a, hipStream_t stream);
+hipError_t launch_combine(const Plan& plan, const Args& a, hipStream_t stream);
+
+}  // namespace mtv

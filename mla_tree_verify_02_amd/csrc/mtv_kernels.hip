@@ -1,0 +1,507 @@
+// gfx950 kernels for absorbed-MLA tree-verify attention over a page_size=1 pool.
+//
+// split_kernel: one workgroup = one key slice of one sequence x up to 64 query
+//   rows (4 waves x 16 rows). Per slice it stages the page indices in LDS, then
+//   streams 32-key tiles through a 3-buffer LDS ring filled by direct
+//   global->LDS 16-byte loads (each 1152-byte latent row is nine full 128-byte
+//   lines), computes S^T = K.Q^T and O^T += V^T.P^T on 16x16x32 bf16 MFMA, and
+//   keeps an online softmax (running max in log2 units, running sum) in fp32.
+//   The pages locate the time of this step in the per-token gather through the
+//   page table ("The 130x Slowdown", The Reasoning, steps 2-5) and ask for a
+//   kernel that reads the prefix without a mask and applies the tree bitmask
+//   only to the tree block ("The Moment of Certainty", The Path Forward; "The
+//   GPU That Wasn't There", The Native Engine Thesis): here the mask test runs
+//   only in tiles that reach the tree block or the end of the sequence.
+// combine_kernel: merges the slices of each row by log-sum-exp and writes the
+//   bf16 output and the natural-log lse.
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+#include <stdint.h>
+
+#include "mtv_internal.h"
+
+namespace mtv {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+#define LDS_AS __attribute__((address_space(3)))
+
+constexpr int kThreads = 256;
+constexpr int kWaves = 4;
+constexpr int kStages = 3;
+constexpr int kChunks = kRowBytes / 16;                          // 72 x 16 B per row
+constexpr int kTileBytes = kTileKeys * kRowBytes;                // 36864
+constexpr int kKeysPerWave = kTileKeys / kWaves;                 // 8 rows loaded per wave
+constexpr int kLoadsPerWave = kKeysPerWave * kChunks / 64;       // 9 loads per wave per tile
+constexpr int kKSteps = kDqk / 32;                               // 18 MFMA k-steps for Q.K^T
+constexpr int kColBlocks = kDv / 16;                             // 32 output column blocks
+constexpr int kPartRowFloats = kDv;                              // floats per row of partial O
+constexpr float kLn2 = 0.6931471805599453f;
+
+static_assert(kKeysPerWave * kChunks % 64 == 0, "tile rows must fill whole wave loads");
+static_assert(kTileKeys == 32, "the P.V k-step covers exactly one tile");
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// One wave-wide 16-byte-per-lane gather straight into LDS: lane i's 16 bytes
+// land at lds_addr + 16 * i (lds_addr wave-uniform, in M0). Issued as inline
+// assembly so that the compiler's wait insertion does not treat every later LDS
+// read as dependent on it; completion is tracked by the explicit vmcnt waits in
+// the tile loop, and the "memory" clobber keeps LDS accesses in program order.
+// M0 is written here and nowhere else in these kernels (gfx9 LDS instructions
+// do not read it), so clobbering it loses nothing.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void gather16_to_lds(const void* src, uint32_t lds_addr)
+{
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                 :
+                 : "v"(src), "s"(lds_addr)
+                 : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// Chunk permutation of tile row `key`: physical 16-byte slot of logical chunk c
+// is c ^ swz(key) (an involution inside each 128-byte band). It spreads both the
+// K-operand reads (16 rows, one chunk) and the transposed V-operand reads (4 rows,
+// two adjacent chunks) over distinct banks.
+__device__ __forceinline__ int swz(int key)
+{
+    return key & 7;
+}
+
+__global__ __launch_bounds__(kThreads, 1) void split_kernel(Args a, int splits, int chunk,
+                                                            int row_groups, float scale_log2)
+{
+    __shared__ __attribute__((aligned(16))) char s_kv[kStages * kTileBytes];
+    __shared__ int s_idx[kMaxChunk];
+
+    const int split = blockIdx.x;
+    const int grp = blockIdx.y;
+    const int b = blockIdx.z;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int rl = lane & 15;   // row (and key) within a 16-block
+    const int lg = lane >> 4;   // lane group 0..3
+    const int N = a.nodes;
+    const int H = a.heads;
+    const int R = N * H;
+
+    const int S = min(max(a.seq_lens[b], N), a.max_kv);
+    const int k0 = split * chunk;
+    if (k0 >= S)
+        return;  // the whole workgroup: this slice lies past the sequence
+    const int nkeys = min(chunk, S - k0);
+    const int ntiles = (nkeys + kTileKeys - 1) / kTileKeys;
+
+    // Stage the slice's page indices. Positions past the end reuse the last
+    // valid position's row (finite data, weight zero); indices are clamped so
+    // that no gather leaves the pool.
+    {
+        const int32_t* pt = a.page_table + (int64_t)b * a.max_kv;
+        const int maxslot = (int)(a.num_slots - 1);
+        for (int i = tid; i < ntiles * kTileKeys; i += kThreads) {
+            int v = pt[min(k0 + i, S - 1)];
+            s_idx[i] = v < 0 ? 0 : (v > maxslot ? maxslot : v);
+        }
+    }
+
+    // This lane's query row: fragments of Q as the B operand of S^T = K.Q^T.
+    const int row = grp * kRowsPerGroup + wave * 16 + rl;
+    const bool row_ok = row < R;
+    const __bf16* qrow = (const __bf16*)a.q + ((int64_t)b * R + (row_ok ? row : 0)) * kDqk;
+    bf16x8 qf[kKSteps];
+#pragma unroll
+    for (int s = 0; s < kKSteps; ++s) {
+        bf16x8 v = *(const bf16x8*)(qrow + (4 * s + lg) * 8);
+        if (!row_ok)
+            v = bf16x8{};
+        qf[s] = v;
+    }
+    const int node = (row_ok ? row : 0) / H;
+    const int W = (N + 31) >> 5;
+    const uint32_t* mrow = a.tree_mask + ((int64_t)b * N + node) * W;
+    const uint32_t mw0 = mrow[0];
+    const uint32_t mw1 = W > 1 ? mrow[1] : 0u;
+    const int tree0 = S - N;  // first key position holding a tree node
+
+    __syncthreads();  // indices staged
+
+    const uint32_t lds0 = (uint32_t)(uintptr_t)(LDS_AS char*)s_kv;
+    const char* kv = (const char*)a.kv;
+
+    // Gather plan of this lane: wave w fills tile rows 8w..8w+7 with nine
+    // wave-wide 1024-byte loads; load j puts lane l's 16 bytes at row
+    // kl = (64j + l) / 72, slot (64j + l) % 72, which holds logical chunk
+    // slot ^ swz(kl). Every aligned 8-lane group covers one full 128-byte band.
+    int gkl[kLoadsPerWave];
+    int gco[kLoadsPerWave];
+#pragma unroll
+    for (int j = 0; j < kLoadsPerWave; ++j) {
+        const int z = j * 64 + lane;
+        gkl[j] = z / kChunks;
+        gco[j] = ((z - gkl[j] * kChunks) ^ swz(gkl[j])) * 16;
+    }
+    // Page indices of the rows this lane gathers for a tile, read from LDS one
+    // tile ahead of the gathers that use them.
+    auto load_idx = [&](int t, int* out) {
+        const int* tidx = s_idx + t * kTileKeys + wave * kKeysPerWave;
+#pragma unroll
+        for (int j = 0; j < kLoadsPerWave; ++j)
+            out[j] = tidx[gkl[j]];
+    };
+    auto issue = [&](int t, const int* idx) {
+        const uint32_t dst = lds0 + (uint32_t)((t % kStages) * kTileBytes +
+                                               wave * (kKeysPerWave * kRowBytes));
+#pragma unroll
+        for (int j = 0; j < kLoadsPerWave; ++j)
+            gather16_to_lds(kv + (int64_t)idx[j] * kRowBytes + gco[j], dst + j * 1024);
+    };
+
+    // Per-lane LDS byte offsets inside a tile buffer; everything else is an
+    // instruction immediate.
+    //  K operand (row rl of key block kb, chunk 4s+lg): (s odd ? koff1 : koff0)
+    //    + kb*16 rows + 128*(s/2)
+    const int fk = swz(rl);
+    const int koff0 = rl * kRowBytes + 16 * (lg ^ fk);
+    const int koff1 = rl * kRowBytes + 16 * ((4 + lg) ^ fk);
+    //  V^T operand (transposed 8-byte reads): lane (lg, rl) reads tile row
+    //  4lg + rl/4 (and +16), columns 16cb + 4(rl%4) .. +3, i.e. chunk
+    //  2cb + (rl%4)/2, half rl%2: voff[cb%4] + 128*(cb/4) (+16 rows)
+    const int vkey = 4 * lg + (rl >> 2);
+    const int fv = swz(vkey);
+    const int vsel = (rl & 3) >> 1;
+    int voff[4];
+#pragma unroll
+    for (int qd = 0; qd < 4; ++qd)
+        voff[qd] = vkey * kRowBytes + 16 * ((2 * qd + vsel) ^ fv) + (rl & 1) * 8;
+
+    f32x4 o[kColBlocks];
+#pragma unroll
+    for (int cb = 0; cb < kColBlocks; ++cb)
+        o[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // Reference max m_ref (log2 units, shared by the row's four lanes) and this
+    // lane's share of the running sum. Weights are 2^(x - m_ref); the reference
+    // is raised only when a tile's max exceeds it by more than kSlack, so weights
+    // stay below 2^kSlack. Raising it rescales O, which happens outside the
+    // steady-state loop (at the first tile and whenever scores jump by more than
+    // kSlack), so the hot loop touches O only through MFMA accumulation.
+    constexpr float kSlack = 16.0f;
+    float m_ref = -INFINITY;
+    float l_run = 0.f;
+
+    // Q fragments and mask words must be in registers before the gathers start:
+    // past this point the only outstanding vector-memory operations are gathers.
+    wait_vmcnt<0>();
+    int idx_n[kLoadsPerWave];  // page indices of the next tile to gather
+    load_idx(0, idx_n);
+    issue(0, idx_n);
+    if (ntiles > 1) {
+        load_idx(1, idx_n);
+        issue(1, idx_n);
+    }
+    if (ntiles > 2)
+        load_idx(2, idx_n);
+
+    constexpr int kKGroup = 6;            // K-operand reads per group (double-buffered)
+    constexpr int kKReads = 2 * kKSteps;  // 36 per tile (two key blocks)
+    constexpr int kVGroup = 4;            // column blocks per V-operand group
+
+    // Tile t's rows are in LDS once this wave's gathers have drained down to the
+    // later tiles' and every wave has passed the barrier; the barrier also frees
+    // the buffer of tile t-1 for the gathers of tile t+2.
+    auto next_tile = [&](int t) {
+        if (t + 1 < ntiles)
+            wait_vmcnt<kLoadsPerWave>();
+        else
+            wait_vmcnt<0>();
+        __syncthreads();
+        if (t + 2 < ntiles)
+            issue(t + 2, idx_n);
+        if (t + 3 < ntiles)
+            load_idx(t + 3, idx_n);
+    };
+
+    int t = 0;
+    next_tile(0);
+    while (true) {
+        float x[8];
+        float mt;
+        for (;;) {
+            const char LDS_AS* buf = (const char LDS_AS*)s_kv + (t % kStages) * kTileBytes;
+            const char LDS_AS* kb0 = buf + koff0;
+            const char LDS_AS* kb1 = buf + koff1;
+            const int base = k0 + t * kTileKeys;
+
+            // S^T = K.Q^T for key blocks 0 and 1 (keys kb*16 + 4*lg + i against
+            // row rl), two interleaved MFMA chains fed by double-buffered groups
+            // of LDS reads. Read n covers k-step n/2 of key block n%2.
+            auto kptr = [&](int n) {
+                const int s = n >> 1;
+                return ((s & 1) ? kb1 : kb0) + (n & 1) * 16 * kRowBytes + 128 * (s >> 1);
+            };
+            bf16x8 kf[2][kKGroup];
+#pragma unroll
+            for (int j = 0; j < kKGroup; ++j)
+                kf[0][j] = *(const bf16x8 LDS_AS*)kptr(j);
+            f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+            for (int g = 0; g < kKReads / kKGroup; ++g) {
+                if (g + 1 < kKReads / kKGroup) {
+#pragma unroll
+                    for (int j = 0; j < kKGroup; ++j)
+                        kf[(g + 1) & 1][j] =
+                            *(const bf16x8 LDS_AS*)kptr((g + 1) * kKGroup + j);
+                }
+#pragma unroll
+                for (int j = 0; j < kKGroup; ++j) {
+                    const int n = g * kKGroup + j;
+                    sacc[n & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        kf[g & 1][j], qf[n >> 1], sacc[n & 1], 0, 0, 0);
+                }
+            }
+
+            // first V^T group in flight while the softmax runs
+            auto vptr = [&](int cb) { return buf + voff[cb & 3] + 128 * (cb >> 2); };
+            bf16x4 vt[2][2 * kVGroup];
+#pragma unroll
+            for (int c = 0; c < kVGroup; ++c) {
+                vt[0][2 * c] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((bf16x4 LDS_AS*)vptr(c));
+                vt[0][2 * c + 1] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                    (bf16x4 LDS_AS*)(vptr(c) + 16 * kRowBytes));
+            }
+
+#pragma unroll
+            for (int k = 0; k < 8; ++k)
+                x[k] = sacc[k >> 2][k & 3] * scale_log2;
+
+            // keep six K-operand reads in flight ahead of the Q.K^T MFMAs
+            __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+#pragma unroll
+            for (int i = 0; i < 30; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, 6, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+            if (base + kTileKeys > tree0) {
+                // tail tile: tree bitmask and the end of the sequence
+#pragma unroll
+                for (int k = 0; k < 8; ++k) {
+                    const int p = base + (k >> 2) * 16 + 4 * lg + (k & 3);
+                    bool vis = p < tree0;
+                    if (p >= tree0 && p < S) {
+                        const int j = p - tree0;
+                        vis = (((j < 32) ? mw0 : mw1) >> (j & 31)) & 1u;
+                    }
+                    if (!vis)
+                        x[k] = -INFINITY;
+                }
+            }
+
+            // This lane's largest score; whether any exceeds the reference by
+            // more than kSlack decides the (rare) rescale. The row's exact max
+            // over its four lanes is only formed on that path.
+            mt = x[0];
+#pragma unroll
+            for (int k = 1; k < 8; ++k)
+                mt = fmaxf(mt, x[k]);
+            if (__builtin_amdgcn_ballot_w64(mt > m_ref + kSlack) != 0)
+                break;  // raise the reference first (outside this loop)
+
+            const float mr = (m_ref == -INFINITY) ? 0.f : m_ref;
+            bf16x8 pb;
+            float psum = 0.f;
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const float pk = exp2f(x[k] - mr);
+                psum += pk;
+                pb[k] = (__bf16)pk;
+            }
+            l_run += psum;
+
+            // O^T[col][row] += V^T[col][key] . P^T[key][row]; the k order of the
+            // MFMA is keys (4lg..4lg+3, 16+4lg..16+4lg+3), matching pb.
+#pragma unroll
+            for (int g = 0; g < kColBlocks / kVGroup; ++g) {
+                if (g + 1 < kColBlocks / kVGroup) {
+#pragma unroll
+                    for (int c = 0; c < kVGroup; ++c) {
+                        const int cb = (g + 1) * kVGroup + c;
+                        vt[(g + 1) & 1][2 * c] =
+                            __builtin_amdgcn_ds_read_tr16_b64_v4bf16((bf16x4 LDS_AS*)vptr(cb));
+                        vt[(g + 1) & 1][2 * c + 1] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                            (bf16x4 LDS_AS*)(vptr(cb) + 16 * kRowBytes));
+                    }
+                }
+#pragma unroll
+                for (int c = 0; c < kVGroup; ++c) {
+                    const int cb = g * kVGroup + c;
+                    const bf16x8 va = __builtin_shufflevector(
+                        vt[g & 1][2 * c], vt[g & 1][2 * c + 1], 0, 1, 2, 3, 4, 5, 6, 7);
+                    o[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb, o[cb], 0, 0, 0);
+                }
+            }
+
+            // two transposed V reads per P.V MFMA, eight ahead
+#pragma unroll
+            for (int i = 0; i < 28; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, 4, 1);
+            if (++t >= ntiles)
+                break;
+            next_tile(t);
+        }
+        if (t >= ntiles)
+            break;
+        // Some row of this wave outgrew its reference on tile t: raise every
+        // row's reference to its running max, rescale, and redo tile t.
+        mt = fmaxf(mt, __shfl_xor(mt, 16));
+        mt = fmaxf(mt, __shfl_xor(mt, 32));
+        const float m_new = fmaxf(m_ref, mt);
+        const float alpha = (m_ref == -INFINITY) ? 0.f : exp2f(m_ref - m_new);
+        m_ref = m_new;
+        l_run *= alpha;
+#pragma unroll
+        for (int cb = 0; cb < kColBlocks; ++cb)
+            o[cb] *= alpha;
+    }
+
+    // Partial result of this slice, in the register-fragment order.
+    float l_tot = l_run + __shfl_xor(l_run, 16);
+    l_tot += __shfl_xor(l_tot, 32);
+    const size_t pidx = ((size_t)b * row_groups + grp) * splits + split;
+    float* po = a.part_o + pidx * (size_t)(kRowsPerGroup * kPartRowFloats) +
+                (size_t)wave * (kColBlocks * 64 * 4);
+#pragma unroll
+    for (int cb = 0; cb < kColBlocks; ++cb)
+        *(f32x4*)(po + (cb * 64 + lane) * 4) = o[cb];
+    if (lg == 0) {
+        float2* pm = (float2*)a.part_ml + pidx * kRowsPerGroup + wave * 16 + rl;
+        *pm = make_float2(m_ref, l_tot);
+    }
+}
+
+// One workgroup per (sequence, 16-row block, 16-column block). Wave w merges
+// slices w, w+4, w+8, ... of its fragment lanes in one pass (running max and
+// rescaled sums), the four waves then merge through LDS, and wave 0 writes the
+// bf16 output (16 rows x 16 columns) and, for column block 0, the lse.
+__global__ __launch_bounds__(kThreads) void combine_kernel(Args a, int splits, int chunk,
+                                                           int row_groups)
+{
+    __shared__ float s_m[kWaves][64];
+    __shared__ float s_l[kWaves][64];
+    __shared__ f32x4 s_o[kWaves][64];
+
+    const int cb = blockIdx.x;           // column block 0..31
+    const int rb = blockIdx.y;           // 16-row block within the sequence
+    const int b = blockIdx.z;
+    const int grp = rb >> 2;
+    const int w = rb & 3;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int rl = lane & 15;
+    const int N = a.nodes;
+    const int R = N * a.heads;
+    const int row = grp * kRowsPerGroup + w * 16 + rl;
+
+    const int S = min(max(a.seq_lens[b], N), a.max_kv);
+    const int nvalid = min(splits, (S + chunk - 1) / chunk);
+    const size_t pbase = ((size_t)b * row_groups + grp) * splits;
+    const float2* pml = (const float2*)a.part_ml + pbase * kRowsPerGroup + w * 16 + rl;
+    const float* pob = a.part_o + pbase * (size_t)(kRowsPerGroup * kPartRowFloats) +
+                       (size_t)w * (kColBlocks * 64 * 4) + (cb * 64 + lane) * 4;
+
+    float M = -INFINITY;
+    float L = 0.f;
+    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+    constexpr int kUnroll = 4;  // slices in flight per wave
+    for (int s0 = wave; s0 < nvalid; s0 += kWaves * kUnroll) {
+        float2 ml[kUnroll];
+        f32x4 o[kUnroll];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const int s = s0 + u * kWaves;
+            const bool in = s < nvalid;
+            const size_t ss = in ? (size_t)s : 0;
+            ml[u] = pml[ss * kRowsPerGroup];
+            o[u] = *(const f32x4*)(pob + ss * (kRowsPerGroup * kPartRowFloats));
+            if (!in)
+                ml[u].x = -INFINITY;
+        }
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            if (ml[u].x == -INFINITY)
+                continue;  // nothing visible to this row in that slice (or past the end)
+            const float mn = fmaxf(M, ml[u].x);
+            const float ca = exp2f(M - mn);  // 0 while M is still -inf
+            const float cs = exp2f(ml[u].x - mn);
+            L = L * ca + ml[u].y * cs;
+            acc = acc * ca + o[u] * cs;
+            M = mn;
+        }
+    }
+    s_m[wave][lane] = M;
+    s_l[wave][lane] = L;
+    s_o[wave][lane] = acc;
+    __syncthreads();
+    if (wave != 0)
+        return;
+    float Mt = s_m[0][lane];
+#pragma unroll
+    for (int k = 1; k < kWaves; ++k)
+        Mt = fmaxf(Mt, s_m[k][lane]);
+    const float mref = (Mt == -INFINITY) ? 0.f : Mt;
+    float Lt = 0.f;
+    f32x4 ot = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k = 0; k < kWaves; ++k) {
+        const float c = exp2f(s_m[k][lane] - mref);  // 0 for waves that saw nothing
+        Lt += s_l[k][lane] * c;
+        ot += s_o[k][lane] * c;
+    }
+    if (row >= R)
+        return;
+    const float inv = Lt > 0.f ? 1.f / Lt : 0.f;
+    bf16x4 v;
+    v[0] = (__bf16)(ot[0] * inv);
+    v[1] = (__bf16)(ot[1] * inv);
+    v[2] = (__bf16)(ot[2] * inv);
+    v[3] = (__bf16)(ot[3] * inv);
+    __bf16* orow = (__bf16*)a.out + ((size_t)b * R + row) * kDv;
+    *(bf16x4*)(orow + 16 * cb + 4 * (lane >> 4)) = v;
+    if (cb == 0 && lane < 16)
+        a.lse[(size_t)b * R + row] = Lt > 0.f ? (Mt + log2f(Lt)) * kLn2 : -INFINITY;
+}
+
+}  // namespace
+
+hipError_t launch_split(const Plan& p, const Args& a, hipStream_t stream)
+{
+    const float scale_log2 = (float)((double)a.scale * 1.4426950408889634);
+    hipLaunchKernelGGL(split_kernel, dim3(p.splits, p.row_groups, a.batch), dim3(kThreads), 0,
+                       stream, a, p.splits, p.chunk, p.row_groups, scale_log2);
+    return hipGetLastError();
+}
+
+hipError_t launch_combine(const Plan& p, const Args& a, hipStream_t stream)
+{
+    hipLaunchKernelGGL(combine_kernel, dim3(kColBlocks, p.row_groups * 4, a.batch), dim3(kThreads),
+                       0, stream, a, p.splits, p.chunk, p.row_groups);
+    return hipGetLastError();
+}
+
+}  // namespace mtv

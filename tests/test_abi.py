@@ -1,0 +1,113 @@
+"""The C ABI without a GPU: the library loads, exports what the header
+declares, and rejects bad host-side arguments before touching a device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import mla_tree_verify_02_amd as M
+from mla_tree_verify_02_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mla_tree_verify.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[A-Za-z_][\w\s\*]*?\b([a-z_][a-z0-9_]*)\s*\(",
+                                 text, flags=re.M)))
+
+
+def test_header_declares_expected_entry_points():
+    assert set(declared_functions()) == set(_lib.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = M.load()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings():
+    for code in (0, -1, -2, -3, -4, -5):
+        assert M.status_string(code) and M.status_string(code) != "unknown status"
+    assert M.status_string(-99) == "unknown status"
+
+
+@pytest.mark.parametrize("shape,ok", [
+    ((1, 8, 8, 1032, 4096), True),
+    ((8, 64, 64, 131136, 1 << 21), True),
+    ((0, 8, 8, 1032, 4096), False),       # no sequences
+    ((1, 0, 8, 1032, 4096), False),       # no tree
+    ((1, 65, 8, 1032, 4096), False),      # more than two mask words
+    ((1, 8, 0, 1032, 4096), False),
+    ((1, 64, 1025, 1032, 4096), False),   # more than 65536 query rows
+    ((1, 8, 8, 7, 4096), False),          # max_kv below the tree size
+    ((1, 8, 8, 1032, 0), False),
+    ((1, 8, 8, 1032, 1 << 31), False),    # slot indices are int32
+])
+def test_workspace_size_validates_shape(shape, ok):
+    ws = M.workspace_size(M.make_shape(*shape))
+    assert (ws > 0) == ok
+
+
+@pytest.mark.parametrize("b,n,h,max_kv,cus", [
+    (1, 8, 8, 1032, 256), (1, 16, 8, 65552, 256), (1, 64, 64, 131136, 256),
+    (8, 8, 8, 131080, 256), (1, 8, 8, 189448, 256), (1, 1, 1, 1, 256), (3, 9, 8, 777, 32),
+])
+def test_plan_covers_every_key(b, n, h, max_kv, cus):
+    p = M.plan_query(M.make_shape(b, n, h, max_kv, 1 << 20), cus)
+    assert p["chunk"] % 32 == 0 and 32 <= p["chunk"] <= 8192
+    assert p["splits"] * p["chunk"] >= max_kv
+    assert (p["splits"] - 1) * p["chunk"] < max_kv
+    assert p["row_groups"] == (n * h + 63) // 64
+
+
+def _call(shape, ptrs=None, ws_bytes=1 << 30, scale=0.07):
+    lib = M.load()
+    good = 1 << 20  # a 256-byte-aligned stand-in address; never dereferenced on the host
+    p = dict(q=good, kv=good, pt=good, sl=good, tm=good, out=good, lse=good, ws=good)
+    if ptrs:
+        p.update(ptrs)
+    V = ctypes.c_void_p
+    return lib.mla_tree_verify(ctypes.byref(shape), V(p["q"]), V(p["kv"]), V(p["pt"]),
+                               V(p["sl"]), V(p["tm"]), ctypes.c_float(scale), V(p["out"]),
+                               V(p["lse"]), V(p["ws"]), ctypes.c_size_t(ws_bytes), None)
+
+
+def test_null_pointers_rejected():
+    s = M.make_shape(1, 8, 8, 1032, 4096)
+    for k in ("q", "kv", "pt", "sl", "tm", "out", "lse", "ws"):
+        assert _call(s, {k: None}) == -1, k
+    assert M.load().mla_tree_verify(None, None, None, None, None, None, ctypes.c_float(1.0),
+                                    None, None, None, 0, None) == -1
+
+
+def test_bad_shape_and_scale_rejected():
+    assert _call(M.make_shape(1, 65, 8, 1032, 4096)) == -2
+    assert _call(M.make_shape(1, 8, 8, 1032, 4096), scale=float("nan")) == -2
+    assert _call(M.make_shape(1, 8, 8, 1032, 4096), scale=float("inf")) == -2
+
+
+def test_misalignment_rejected():
+    s = M.make_shape(1, 8, 8, 1032, 4096)
+    base = 1 << 20
+    for k, off in (("q", 8), ("kv", 2), ("out", 4), ("pt", 2), ("sl", 1), ("tm", 2),
+                   ("lse", 2), ("ws", 64)):
+        assert _call(s, {k: base + off}) == -3, k
+
+
+def test_python_binding_rejects_host_tensors():
+    import torch
+    q = torch.zeros(1, 8, 8, 576, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        M.mla_tree_verify(q, torch.zeros(16, 576, dtype=torch.bfloat16),
+                          torch.zeros(1, 16, dtype=torch.int32), torch.tensor([16], dtype=torch.int32),
+                          torch.zeros(1, 8, 1, dtype=torch.int32), 0.1)
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    with pytest.raises(FileNotFoundError):
+        _lib.load(str(tmp_path / "nope.so"))

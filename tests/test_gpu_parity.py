@@ -1,0 +1,230 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Tolerance (elementwise, compared in fp32): out |g - o| <= 2e-2 + 2e-2 |o|;
+lse |g - o| <= 1e-3 + 1e-3 |o|. Page-index and mask handling are checked bit
+for bit: a relayout of the same logical rows, poisoned rows that a node may not
+see and junk past the sequence end must leave the output bits unchanged.
+At long context N(0,1) outputs shrink towards the absolute tolerance, so every
+long case also runs a "peaked" variant (Q x 4, exact in bf16) with O(0.1-1)
+outputs.
+"""
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import mla_tree_verify_02_amd as M
+from mla_tree_verify_02_amd import inputs as I
+
+pytestmark = pytest.mark.gpu
+
+OUT_TOL = 2e-2
+LSE_TOL = 1e-3
+
+
+@pytest.fixture(scope="module", autouse=True)
+def need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    M.load()  # raises if the HIP library was not built
+
+
+def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    return (bits.astype(np.uint32) << 16).view(np.float32)
+
+
+def run_gpu(wl):
+    out, lse = M.verify_workload(wl)
+    torch.cuda.synchronize()
+    return (out.view(torch.int16).cpu().numpy().view(np.uint16),
+            lse.cpu().numpy())
+
+
+def compare(wl, oracle_mod, rows=None, label=""):
+    """Run both sides; compare all rows or the given flat row ids."""
+    g_out, g_lse = run_gpu(wl)
+    o_out, o_lse = oracle_mod.run_workload(wl, rows=rows)
+    g_out = bf16_bits_to_f32(g_out).reshape(-1, 512)
+    o_out = bf16_bits_to_f32(o_out).reshape(-1, 512)
+    g_lse = g_lse.reshape(-1)
+    o_lse = o_lse.reshape(-1)
+    sel = np.arange(g_lse.size) if rows is None else np.asarray(rows)
+    go, oo = g_out[sel].astype(np.float64), o_out[sel].astype(np.float64)
+    gl, ol = g_lse[sel].astype(np.float64), o_lse[sel].astype(np.float64)
+    assert np.isfinite(go).all(), f"{label}: non-finite GPU output"
+    err_o = np.abs(go - oo)
+    err_l = np.where(np.isinf(ol) & np.isinf(gl) & (np.sign(ol) == np.sign(gl)), 0.0, np.abs(gl - ol))
+    rel_fro = float(np.linalg.norm(go - oo) / max(np.linalg.norm(oo), 1e-30))
+    print(f"[{label}] rows={len(sel)} max|dout|={err_o.max():.3e} rel_fro={rel_fro:.3e} "
+          f"max|dlse|={err_l.max():.3e} max|out|={np.abs(oo).max():.3f}", flush=True)
+    assert (err_o <= OUT_TOL + OUT_TOL * np.abs(oo)).all(), f"{label}: out outside tolerance"
+    assert (err_l <= LSE_TOL + LSE_TOL * np.abs(ol)).all(), f"{label}: lse outside tolerance"
+    return g_out, g_lse
+
+
+def sample_rows(wl, k, seed=0):
+    total = wl.batch * wl.num_nodes * wl.num_heads
+    rng = np.random.default_rng(seed)
+    return np.unique(np.concatenate([[0, total - 1], rng.choice(total, size=min(k, total), replace=False)]))
+
+
+# ----------------------------------------------------------- small, all rows
+
+@pytest.mark.parametrize("q_gain", [1.0, 4.0])
+def test_tiny_chain_all_rows(oracle_mod, q_gain):
+    wl = I.config_workload(1, device="cuda", q_gain=q_gain)
+    compare(wl, oracle_mod, label=f"chain8 ctx1024 gain{q_gain}")
+
+
+@pytest.mark.parametrize("case", [
+    dict(batch=1, num_nodes=9, num_heads=8, prefix_lens=[700], tree="random", max_depth=4),   # 72 rows
+    dict(batch=1, num_nodes=16, num_heads=8, prefix_lens=[2000], tree="binary"),               # 128 rows
+    dict(batch=3, num_nodes=5, num_heads=3, prefix_lens=[0, 31, 1000], tree="random", max_depth=3),
+    dict(batch=2, num_nodes=64, num_heads=2, prefix_lens=[100, 4097], tree="random", max_depth=8),
+    dict(batch=1, num_nodes=1, num_heads=1, prefix_lens=[0], tree="chain"),                    # one key
+    dict(batch=2, num_nodes=8, num_heads=8, prefix_lens=[8191, 8193], tree="chain"),           # chunk edges
+])
+def test_small_shapes_all_rows(oracle_mod, case):
+    wl = I.make_workload(num_slots=32768, config_id=100, device="cuda", **case)
+    compare(wl, oracle_mod, label=str(case))
+
+
+@pytest.mark.parametrize("n", [31, 32, 33, 64])
+def test_random_bitmasks_word_boundaries(oracle_mod, n):
+    m = I.random_bitmask(n, seed=500 + n, density=0.4)
+    m[1, :] = 0  # node 1 sees only the prefix
+    wl = I.make_workload(batch=1, num_nodes=n, num_heads=4, prefix_lens=[77], num_slots=4096,
+                         tree="chain", config_id=101, mask=m, device="cuda")
+    compare(wl, oracle_mod, label=f"random bits n={n}")
+
+
+def test_empty_visible_set(oracle_mod):
+    m = np.array([[0], [3]], dtype=np.uint32)
+    wl = I.make_workload(batch=1, num_nodes=2, num_heads=2, prefix_lens=[0], num_slots=64,
+                         tree="chain", config_id=102, mask=m, device="cuda")
+    g_out, g_lse = run_gpu(wl)
+    assert np.all(g_out[0, 0] == 0) and np.all(np.isneginf(g_lse[0, 0]))
+    compare(wl, oracle_mod, label="empty visible set")
+
+
+# ---------------------------------------------------- bit-exact index / mask handling
+
+def relayout_gpu(wl, table_seed, layout):
+    other = I.make_workload(batch=wl.batch, num_nodes=wl.num_nodes, num_heads=wl.num_heads,
+                            prefix_lens=wl.prefix_lens, num_slots=wl.num_slots, tree="chain",
+                            layout=layout, table_seed=table_seed, config_id=103,
+                            mask=wl.np_mask(), device="cuda")
+    other.q = wl.q.clone()
+    kv_new = torch.full_like(wl.kv_pool.view(torch.int16), I.BF16_NAN_BITS)
+    t_old, t_new = wl.page_table.long(), other.page_table.long()
+    for b, S in enumerate(wl.seq_lens_host()):
+        kv_new[t_new[b, :S]] = wl.kv_pool.view(torch.int16)[t_old[b, :S]]
+    other.kv_pool = kv_new.view(torch.bfloat16)
+    return other
+
+
+def test_layout_invariance_bitwise():
+    wl = I.make_workload(batch=3, num_nodes=8, num_heads=8, prefix_lens=[5000, 77, 12345],
+                         num_slots=65536, tree="random", max_depth=5, config_id=104, device="cuda")
+    ref = run_gpu(wl)
+    for seed, layout in [(11, "scattered"), (12, "runs64")]:
+        got = run_gpu(relayout_gpu(wl, seed, layout))
+        assert np.array_equal(got[0], ref[0])
+        assert np.array_equal(got[1].view(np.uint32), ref[1].view(np.uint32))
+
+
+def test_repeat_runs_bitwise():
+    wl = I.config_workload(1, device="cuda")
+    a = run_gpu(wl)
+    b = run_gpu(wl)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_masked_tree_rows_do_not_leak():
+    n, h, ctx = 8, 8, 3000
+    wl = I.make_workload(batch=1, num_nodes=n, num_heads=h, prefix_lens=[ctx], num_slots=8192,
+                         tree="chain", config_id=105, device="cuda")
+    base = run_gpu(wl)
+    slot = int(wl.page_table[0, ctx + n - 1].item())  # seen by node n-1 only
+    poison = torch.tensor([1e4 if c % 2 == 0 else -1e4 for c in range(576)], device="cuda")
+    wl.kv_pool[slot] = poison.to(torch.bfloat16)
+    got = run_gpu(wl)
+    assert np.array_equal(got[0][0, :n - 1], base[0][0, :n - 1])
+    assert np.array_equal(got[1][0, :n - 1], base[1][0, :n - 1])
+    assert not np.array_equal(got[0][0, n - 1], base[0][0, n - 1])
+
+
+def test_positions_past_seq_len_are_not_read():
+    wl = I.make_workload(batch=2, num_nodes=8, num_heads=8, prefix_lens=[100, 33], num_slots=4096,
+                         tree="chain", config_id=106, max_kv=4000, device="cuda")
+    base = run_gpu(wl)
+    t = wl.page_table.clone()
+    t[0, 108:] = 10 ** 9   # out of range: must never be gathered
+    t[1, 41:] = -7
+    wl.page_table = t
+    got = run_gpu(wl)
+    assert np.array_equal(got[0], base[0]) and np.array_equal(got[1], base[1])
+
+
+# ------------------------------------------------------------ full-size configs
+
+@pytest.mark.parametrize("q_gain", [1.0, 4.0])
+def test_binary16_ctx65536(oracle_mod, q_gain):
+    wl = I.config_workload(2, device="cuda", q_gain=q_gain)
+    compare(wl, oracle_mod, label=f"binary16 ctx65536 gain{q_gain}")
+
+
+@pytest.mark.parametrize("ctx", [11264, 189440])
+def test_chain8_sweep_points(oracle_mod, ctx):
+    for layer, gain in ((0, 1.0), (60, 4.0)):
+        wl = I.config_workload(3, device="cuda", ctx=ctx, layer=layer, q_gain=gain)
+        compare(wl, oracle_mod, rows=sample_rows(wl, 24, seed=layer),
+                label=f"chain8 ctx{ctx} layer{layer} gain{gain}")
+
+
+def test_random64_h64_ctx131072(oracle_mod):
+    wl = I.config_workload(4, device="cuda", q_gain=4.0)
+    compare(wl, oracle_mod, rows=sample_rows(wl, 48, seed=4), label="random64 h64 ctx131072")
+
+
+def test_batch8_both_layouts(oracle_mod):
+    a = I.config_workload(5, device="cuda", layout="scattered")
+    g_a = compare(a, oracle_mod, rows=sample_rows(a, 40, seed=5), label="batch8 scattered")
+    b = relayout_gpu(a, I.seed_for(5, 0, I.F_TABLE) + 1, "runs64")
+    ga = run_gpu(a)
+    gb = run_gpu(b)
+    assert np.array_equal(ga[0], gb[0]) and np.array_equal(ga[1], gb[1])
+
+
+# ------------------------------------------------------------------ graph capture
+
+def test_graph_capture_replays_match_eager():
+    wl = I.make_workload(batch=2, num_nodes=16, num_heads=8, prefix_lens=[3000, 9000],
+                         num_slots=32768, tree="binary", config_id=107, device="cuda")
+    eager_out, eager_lse = M.verify_workload(wl)
+    torch.cuda.synchronize()
+    eager = (eager_out.clone(), eager_lse.clone())
+    shape = M.make_shape(wl.batch, wl.num_nodes, wl.num_heads, wl.max_kv, wl.num_slots)
+    ws = torch.empty(M.workspace_size(shape), dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(eager_out)
+    lse = torch.empty_like(eager_lse)
+    other = I.config_workload(1, device="cuda")
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        M.verify_workload(wl, out=out, lse=lse, workspace=ws)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        M.verify_workload(wl, out=out, lse=lse, workspace=ws)
+    for _ in range(4):
+        out.fill_(0)
+        lse.fill_(0)
+        g.replay()
+        M.verify_workload(other)  # eager work between replays
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), eager[0].view(torch.int16))
+        assert torch.equal(lse, eager[1])
