@@ -33,6 +33,8 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "achieved HBM GB/s (% of peak) for MLA tree-verify at 64k/185k ctx; µs/layer"
+KERNEL_SOURCE = os.path.join(ROOT, "mla_tree_verify_02_amd", "csrc", "mtv_kernels.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "split_kernel_binary16-ctx65536_traffic.json")
 PEAK_GBPS = 8000.0
 LAYERS = 61
 
@@ -47,6 +49,38 @@ def split_kernel_bytes(seq_lens, n, h):
     w = I.mask_words(n)
     return sum(int(s) for s in seq_lens) * (I.ROW_BYTES + 4) + len(seq_lens) * (
         n * h * I.D_QK * 2 + n * w * 4)
+
+
+def kernel_source_hash() -> str:
+    import hashlib
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per split-kernel launch from the committed counter summary, if
+    it was taken on the current kernel source (else None)."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def copy_calibration(mib, torch):
+    """A plain copy of known size (reads and writes mib MiB each), run outside
+    the timed region so that a counter pass can scale FETCH_SIZE/WRITE_SIZE."""
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.mul(src, 1.0, out=dst)
+    torch.cuda.synchronize()
+    log("copy calibration: 3 x %d MiB read + %d MiB written" % (mib, mib))
+    del src, dst
 
 
 def time_calls(calls, steps, warmup, torch):
@@ -147,18 +181,23 @@ def sweep(args, torch, M, I):
     return results
 
 
-def cpu_baseline(wl, call_bytes, I):
+def cpu_baseline(wls, call_bytes, I):
+    """The CPU oracle, as it stands, on a bounded sample: full calls of the
+    headline workload on the first input sets (about 10-30 s of CPU work)."""
     from oracle import oracle as O
     try:
         cores = len(os.sched_getaffinity(0))
     except AttributeError:
         cores = os.cpu_count() or 1
     threads = max(1, min(16, cores))
-    log("CPU oracle on one full call with %d threads" % threads)
-    host = (wl.np_q(), wl.np_kv(), wl.np_page_table(), wl.np_seq_lens(), wl.np_mask())
-    t0 = time.perf_counter()
-    O.run(*host, wl.scale, threads=threads)
-    dt = time.perf_counter() - t0
+    sample = wls[:3]
+    log("CPU oracle on %d full calls with %d threads" % (len(sample), threads))
+    total = 0.0
+    for wl in sample:
+        host = (wl.np_q(), wl.np_kv(), wl.np_page_table(), wl.np_seq_lens(), wl.np_mask())
+        t0 = time.perf_counter()
+        O.run(*host, wl.scale, threads=threads)
+        total += time.perf_counter() - t0
     model = "unknown"
     try:
         with open("/proc/cpuinfo") as f:
@@ -168,10 +207,12 @@ def cpu_baseline(wl, call_bytes, I):
                     break
     except OSError:
         pass
-    return {"value": round(call_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": threads,
-            "kind": "oracle", "seconds": round(dt, 3), "cpu_model": model,
-            "sample": "one full call (all %d rows) of the binary16-ctx65536 workload, input set 0"
-                      % (wl.batch * wl.num_nodes * wl.num_heads)}
+    rows = sample[0].batch * sample[0].num_nodes * sample[0].num_heads
+    return {"value": round(len(sample) * call_bytes / total / 1e9, 4), "unit": "GB/s",
+            "cores": threads, "kind": "oracle", "seconds": round(total, 3),
+            "cpu_model": model,
+            "sample": "%d full calls (all %d rows each) of the binary16-ctx65536 workload, "
+                      "input sets 0-%d" % (len(sample), rows, len(sample) - 1)}
 
 
 def main() -> int:
@@ -184,6 +225,8 @@ def main() -> int:
                     help="contexts of the 61-layer chain8 sweep ('' to skip)")
     ap.add_argument("--sweep-steps", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="also run a plain copy of MIB MiB (for counter calibration)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -205,6 +248,8 @@ def main() -> int:
     props = torch.cuda.get_device_properties(0)
     log("device %s, %d CUs" % (props.name, props.multi_processor_count))
 
+    if args.copy_calibration > 0:
+        copy_calibration(args.copy_calibration, torch)
     hd = headline(args, torch, M, I)
     sec = hd["sec"]
     value = hd["call_bytes"] / sec / 1e9
@@ -213,7 +258,7 @@ def main() -> int:
         % (sec * 1e6, value, hd["split_avg_ms"] * 1e3, hd["split_med_ms"] * 1e3, achieved))
 
     sw = sweep(args, torch, M, I)
-    cpu = None if args.no_cpu_baseline else cpu_baseline(hd["wls"][0], hd["call_bytes"], I)
+    cpu = None if args.no_cpu_baseline else cpu_baseline(hd["wls"], hd["call_bytes"], I)
 
     wl = hd["wls"][0]
     line = {
@@ -239,7 +284,7 @@ def main() -> int:
         "pct_of_peak": round(100 * value / PEAK_GBPS, 2),
         "roofline": {"bound": "hbm", "kernel": "split_kernel",
                      "achieved": round(achieved, 1), "peak": PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(achieved / PEAK_GBPS, 4), "traffic": None,
+                     "frac": round(achieved / PEAK_GBPS, 4), "traffic": measured_traffic(),
                      "avg_launch_us": round(hd["split_avg_ms"] * 1e3, 3),
                      "bytes_per_launch": hd["split_bytes"]},
         "context_sweep": sw,

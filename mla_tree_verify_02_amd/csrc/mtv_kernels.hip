@@ -85,9 +85,17 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(Args a, int splits, 
     __shared__ __attribute__((aligned(16))) char s_kv[kStages * kTileBytes];
     __shared__ int s_idx[kMaxChunk];
 
-    const int split = blockIdx.x;
-    const int grp = blockIdx.y;
-    const int b = blockIdx.z;
+    // XCD-aware order: workgroups are dealt to the eight XCDs round-robin by
+    // id, so ids L and L + 8 share an XCD (and its L2). The row groups of one
+    // key slice get ids 8 apart and consecutive dispatch slots on one XCD,
+    // so all but the first read the slice's rows from that XCD's L2.
+    const int L = blockIdx.x;
+    const int w8 = L >> 3;
+    const int grp = w8 % row_groups;
+    const int split = (w8 / row_groups) * 8 + (L & 7);
+    const int b = blockIdx.y;
+    if (split >= splits)
+        return;  // padding of the slice count to a multiple of 8
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -492,7 +500,8 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(Args a, int splits, i
 hipError_t launch_split(const Plan& p, const Args& a, hipStream_t stream)
 {
     const float scale_log2 = (float)((double)a.scale * 1.4426950408889634);
-    hipLaunchKernelGGL(split_kernel, dim3(p.splits, p.row_groups, a.batch), dim3(kThreads), 0,
+    const int splits8 = (p.splits + 7) / 8 * 8;
+    hipLaunchKernelGGL(split_kernel, dim3(splits8 * p.row_groups, a.batch), dim3(kThreads), 0,
                        stream, a, p.splits, p.chunk, p.row_groups, scale_log2);
     return hipGetLastError();
 }
