@@ -135,9 +135,10 @@ int mla_tree_verify(const mtv_shape* shape,
  *
  * mla_tree_verify_splitkv enqueues only the split-KV kernel: it takes the same
  * inputs as mla_tree_verify and leaves, in `workspace`, one partial per
- * (sequence, 64-row group, key slice): the unnormalised weighted latent sum,
- * the running max of the scaled scores in log2 units and the sum of
- * 2^(score*log2(e) - max). mla_tree_verify_combine merges those partials by
+ * (sequence, 64-row group, key slice): the unnormalised weighted latent sum
+ * (stored as bf16, 1024 B per row), the running max of the scaled scores in
+ * log2 units and the sum of 2^(score*log2(e) - max) (fp32, 8 B per row).
+ * mla_tree_verify_combine merges those partials by
  * log-sum-exp and writes out and lse. The combine must run on a workspace
  * filled by a splitkv call with the same shape on the same device (the layout
  * follows mtv_plan_query), ordered after it on a stream. Arguments, alignment

@@ -68,7 +68,7 @@ mtv::Plan make_plan(const mtv_shape& s, int cus)
     p.chunk = (int)(chunk_tiles * mtv::kTileKeys);
     const size_t parts = (size_t)pairs * (size_t)p.splits;
     p.part_o_off = 0;
-    p.part_ml_off = align_up(parts * mtv::kRowsPerGroup * mtv::kDv * sizeof(float), 256);
+    p.part_ml_off = align_up(parts * mtv::kRowsPerGroup * mtv::kDv * sizeof(uint16_t), 256);
     p.bytes = align_up(p.part_ml_off + parts * mtv::kRowsPerGroup * 2 * sizeof(float), 256);
     return p;
 }
@@ -148,7 +148,7 @@ int run(int phases, const mtv_shape* shape, const void* q, const void* kv_pool,
     a.scale = scale;
     a.out = out;
     a.lse = lse;
-    a.part_o = (float*)((char*)workspace + plan.part_o_off);
+    a.part_o = (uint16_t*)((char*)workspace + plan.part_o_off);
     a.part_ml = (float*)((char*)workspace + plan.part_ml_off);
     a.batch = shape->batch;
     a.nodes = shape->num_nodes;

@@ -34,7 +34,7 @@ struct Args {
     float scale;
     void* out;
     float* lse;
-    float* part_o;   // [B][G][splits][64 rows as 4 waves x 32 col-blocks x 64 lanes x 4]
+    uint16_t* part_o;  // bf16 [B][G][splits][64 rows as 4 waves x 32 col-blocks x 64 lanes x 4]
     float* part_ml;  // [B][G][splits][64 rows][2]  (running max in log2 units, sum)
     int batch, nodes, heads, max_kv;
     int64_t num_slots;

@@ -38,8 +38,11 @@ constexpr int kKeysPerWave = kTileKeys / kWaves;                 // 8 rows loade
 constexpr int kLoadsPerWave = kKeysPerWave * kChunks / 64;       // 9 loads per wave per tile
 constexpr int kKSteps = kDqk / 32;                               // 18 MFMA k-steps for Q.K^T
 constexpr int kColBlocks = kDv / 16;                             // 32 output column blocks
-constexpr int kPartRowFloats = kDv;                              // floats per row of partial O
+constexpr int kPartRowElems = kDv;                               // bf16 elements per row of partial O
 constexpr float kLn2 = 0.6931471805599453f;
+constexpr int kCombineWaves = 8;                                 // waves per combine workgroup
+constexpr int kCombineThreads = kCombineWaves * 64;
+constexpr int kCombineUnroll = 16;                               // slices in flight per wave
 
 static_assert(kKeysPerWave * kChunks % 64 == 0, "tile rows must fill whole wave loads");
 static_assert(kTileKeys == 32, "the P.V k-step covers exactly one tile");
@@ -332,7 +335,10 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(Args a, int splits, 
             float psum = 0.f;
 #pragma unroll
             for (int k = 0; k < 8; ++k) {
-                const float pk = exp2f(x[k] - mr);
+                // hardware 2^x (v_exp_f32): the argument lies in [-inf, kSlack];
+                // results below the smallest normal float (weights under 2^-126
+                // of the reference) flush to zero
+                const float pk = __builtin_amdgcn_exp2f(x[k] - mr);
                 psum += pk;
                 pb[k] = (__bf16)pk;
             }
@@ -391,11 +397,21 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(Args a, int splits, 
     float l_tot = l_run + __shfl_xor(l_run, 16);
     l_tot += __shfl_xor(l_tot, 32);
     const size_t pidx = ((size_t)b * row_groups + grp) * splits + split;
-    float* po = a.part_o + pidx * (size_t)(kRowsPerGroup * kPartRowFloats) +
-                (size_t)wave * (kColBlocks * 64 * 4);
+    // O is stored rounded to bf16 (round to nearest even, relative error at
+    // most 2^-8 per element); the combine scales each slice's O by a factor of
+    // at most 1, so the merged output carries at most that relative error per
+    // slice term. It halves the partial traffic; the running max and sum stay
+    // fp32, so the lse is unaffected.
+    __bf16* po = (__bf16*)a.part_o + pidx * (size_t)(kRowsPerGroup * kPartRowElems) +
+                 (size_t)wave * (kColBlocks * 64 * 4);
 #pragma unroll
-    for (int cb = 0; cb < kColBlocks; ++cb)
-        *(f32x4*)(po + (cb * 64 + lane) * 4) = o[cb];
+    for (int cb = 0; cb < kColBlocks; ++cb) {
+        bf16x4 v;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            v[i] = (__bf16)o[cb][i];
+        *(bf16x4*)(po + (cb * 64 + lane) * 4) = v;
+    }
     if (lg == 0) {
         float2* pm = (float2*)a.part_ml + pidx * kRowsPerGroup + wave * 16 + rl;
         *pm = make_float2(m_ref, l_tot);
@@ -403,15 +419,15 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(Args a, int splits, 
 }
 
 // One workgroup per (sequence, 16-row block, 16-column block). Wave w merges
-// slices w, w+4, w+8, ... of its fragment lanes in one pass (running max and
-// rescaled sums), the four waves then merge through LDS, and wave 0 writes the
-// bf16 output (16 rows x 16 columns) and, for column block 0, the lse.
-__global__ __launch_bounds__(kThreads) void combine_kernel(Args a, int splits, int chunk,
-                                                           int row_groups)
+// slices w, w+8, w+16, ... of its fragment lanes (running max and rescaled
+// sums), the eight waves then merge through LDS, and wave 0 writes the bf16
+// output (16 rows x 16 columns) and, for column block 0, the lse.
+__global__ __launch_bounds__(kCombineThreads) void combine_kernel(Args a, int splits, int chunk,
+                                                                   int row_groups)
 {
-    __shared__ float s_m[kWaves][64];
-    __shared__ float s_l[kWaves][64];
-    __shared__ f32x4 s_o[kWaves][64];
+    __shared__ float s_m[kCombineWaves][64];
+    __shared__ float s_l[kCombineWaves][64];
+    __shared__ f32x4 s_o[kCombineWaves][64];
 
     const int cb = blockIdx.x;           // column block 0..31
     const int rb = blockIdx.y;           // 16-row block within the sequence
@@ -430,37 +446,51 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(Args a, int splits, i
     const int nvalid = min(splits, (S + chunk - 1) / chunk);
     const size_t pbase = ((size_t)b * row_groups + grp) * splits;
     const float2* pml = (const float2*)a.part_ml + pbase * kRowsPerGroup + w * 16 + rl;
-    const float* pob = a.part_o + pbase * (size_t)(kRowsPerGroup * kPartRowFloats) +
-                       (size_t)w * (kColBlocks * 64 * 4) + (cb * 64 + lane) * 4;
+    const __bf16* pob = (const __bf16*)a.part_o + pbase * (size_t)(kRowsPerGroup * kPartRowElems) +
+                        (size_t)w * (kColBlocks * 64 * 4) + (cb * 64 + lane) * 4;
 
+    // Each wave takes every kCombineWaves-th slice and loads kCombineUnroll of
+    // them at once (the whole slice set of a typical split in one round), then
+    // folds them into its running (max, sum, weighted sum) with one exp per
+    // slice against the round's max.
     float M = -INFINITY;
     float L = 0.f;
     f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-    constexpr int kUnroll = 4;  // slices in flight per wave
-    for (int s0 = wave; s0 < nvalid; s0 += kWaves * kUnroll) {
-        float2 ml[kUnroll];
-        f32x4 o[kUnroll];
+    for (int s0 = wave; s0 < nvalid; s0 += kCombineWaves * kCombineUnroll) {
+        float2 ml[kCombineUnroll];
+        f32x4 o[kCombineUnroll];
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-            const int s = s0 + u * kWaves;
+        for (int u = 0; u < kCombineUnroll; ++u) {
+            const int s = s0 + u * kCombineWaves;
             const bool in = s < nvalid;
             const size_t ss = in ? (size_t)s : 0;
             ml[u] = pml[ss * kRowsPerGroup];
-            o[u] = *(const f32x4*)(pob + ss * (kRowsPerGroup * kPartRowFloats));
-            if (!in)
-                ml[u].x = -INFINITY;
-        }
+            const bf16x4 v = *(const bf16x4*)(pob + ss * (kRowsPerGroup * kPartRowElems));
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-            if (ml[u].x == -INFINITY)
-                continue;  // nothing visible to this row in that slice (or past the end)
-            const float mn = fmaxf(M, ml[u].x);
-            const float ca = exp2f(M - mn);  // 0 while M is still -inf
-            const float cs = exp2f(ml[u].x - mn);
-            L = L * ca + ml[u].y * cs;
-            acc = acc * ca + o[u] * cs;
-            M = mn;
+            for (int i = 0; i < 4; ++i)
+                o[u][i] = (float)v[i];
+            if (!in) {
+                ml[u] = make_float2(-INFINITY, 0.f);
+                o[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+            }
         }
+        float mx = M;
+#pragma unroll
+        for (int u = 0; u < kCombineUnroll; ++u)
+            mx = fmaxf(mx, ml[u].x);
+        if (mx == -INFINITY)
+            continue;  // nothing visible to this row so far
+        const float ca = exp2f(M - mx);  // 0 while M is still -inf
+        L *= ca;
+        acc *= ca;
+#pragma unroll
+        for (int u = 0; u < kCombineUnroll; ++u) {
+            // a slice that saw nothing has (m, l, o) = (-inf, 0, 0): weight 0
+            const float cs = exp2f(ml[u].x - mx);
+            L += ml[u].y * cs;
+            acc += o[u] * cs;
+        }
+        M = mx;
     }
     s_m[wave][lane] = M;
     s_l[wave][lane] = L;
@@ -470,13 +500,13 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(Args a, int splits, i
         return;
     float Mt = s_m[0][lane];
 #pragma unroll
-    for (int k = 1; k < kWaves; ++k)
+    for (int k = 1; k < kCombineWaves; ++k)
         Mt = fmaxf(Mt, s_m[k][lane]);
     const float mref = (Mt == -INFINITY) ? 0.f : Mt;
     float Lt = 0.f;
     f32x4 ot = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int k = 0; k < kWaves; ++k) {
+    for (int k = 0; k < kCombineWaves; ++k) {
         const float c = exp2f(s_m[k][lane] - mref);  // 0 for waves that saw nothing
         Lt += s_l[k][lane] * c;
         ot += s_o[k][lane] * c;
@@ -508,7 +538,7 @@ hipError_t launch_split(const Plan& p, const Args& a, hipStream_t stream)
 
 hipError_t launch_combine(const Plan& p, const Args& a, hipStream_t stream)
 {
-    hipLaunchKernelGGL(combine_kernel, dim3(kColBlocks, p.row_groups * 4, a.batch), dim3(kThreads),
+    hipLaunchKernelGGL(combine_kernel, dim3(kColBlocks, p.row_groups * 4, a.batch), dim3(kCombineThreads),
                        0, stream, a, p.splits, p.chunk, p.row_groups);
     return hipGetLastError();
 }
