@@ -13,9 +13,13 @@ Q, out, lse and the mask.
 Also reported on the same line:
   roofline     the split-KV kernel's algorithmic bytes / its average launch
                duration (HIP events around each launch), against 8 TB/s;
+  call_us      p10 / p50 / p90 of per-call durations (HIP events);
   context_sweep the 61-layer stacked chain8 sweep (own pool per layer, one page
                table per context): microseconds per layer and GB/s;
-  cpu_baseline the CPU oracle on one full call of the headline workload.
+  other_configs 64 nodes x 64 heads at context 131072 (MFMA-bound: TFLOP/s
+               against 2.5 PFLOP/s dense bf16) and batch 8 with log-uniform
+               contexts in both page layouts (GB/s each; outputs bitwise equal);
+  cpu_baseline the CPU oracle on full calls of the headline workload.
 
 Prints progress to stderr and one JSON line to stdout.
 """
@@ -36,6 +40,7 @@ METRIC = "achieved HBM GB/s (% of peak) for MLA tree-verify at 64k/185k ctx; µs
 KERNEL_SOURCE = os.path.join(ROOT, "mla_tree_verify_02_amd", "csrc", "mtv_kernels.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "split_kernel_binary16-ctx65536_traffic.json")
 PEAK_GBPS = 8000.0
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 LAYERS = 61
 
 
@@ -112,6 +117,25 @@ def time_split_kernel(calls, steps, torch):
     return sum(ms) / len(ms), ms[len(ms) // 2]
 
 
+def time_each_call(calls, steps, torch, fn="run"):
+    """Per-call durations (us) from HIP events around each call on torch's
+    current stream, rotating over `calls`; returns the sorted list."""
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    torch.cuda.synchronize()
+    for k in range(steps):
+        ev[k][0].record(stream)
+        getattr(calls[k % len(calls)], fn)()
+        ev[k][1].record(stream)
+    torch.cuda.synchronize()
+    return sorted(a.elapsed_time(b) * 1e3 for a, b in ev)
+
+
+def pct(sorted_us, q):
+    return sorted_us[min(len(sorted_us) - 1, int(q * len(sorted_us)))]
+
+
 def headline(args, torch, M, I):
     log("building headline inputs (binary16-ctx65536, %d rotated sets)" % args.rotate)
     wls = [I.config_workload(2, device="cuda", layer=r) for r in range(args.rotate)]
@@ -131,8 +155,82 @@ def headline(args, torch, M, I):
     kbytes = split_kernel_bytes(seq, n, h)
     plan = M.plan_query(M.make_shape(1, n, h, wls[0].max_kv, wls[0].num_slots),
                         torch.cuda.get_device_properties(0).multi_processor_count)
+    per_call = time_each_call(calls, args.steps, torch)
     return dict(wls=wls, sec=sec, call_bytes=call_bytes, split_avg_ms=avg_ms,
-                split_med_ms=med_ms, split_bytes=kbytes, plan=plan)
+                split_med_ms=med_ms, split_bytes=kbytes, plan=plan,
+                call_us={"p10": round(pct(per_call, 0.1), 3), "p50": round(pct(per_call, 0.5), 3),
+                         "p90": round(pct(per_call, 0.9), 3)})
+
+
+def other_configs(args, torch, M, I):
+    """The all-heads configuration (64 nodes x 64 heads, MFMA-bound) and the
+    batch-8 mixed-length configuration in both page layouts."""
+    out = {}
+    names = [c.strip() for c in args.configs.split(",") if c.strip()]
+    if "c4" in names:
+        log("building random64-h64-ctx131072 (2 rotated sets)")
+        wls = [I.config_workload(4, device="cuda", layer=r) for r in range(2)]
+        ws = None
+        calls = []
+        for wl in wls:
+            c = M.prepare_workload(wl, workspace=ws)
+            ws = c.workspace
+            calls.append(c)
+        for c in calls:
+            c.run()
+        us = time_each_call(calls, args.big_steps, torch)
+        sk = time_each_call(calls, args.big_steps, torch, "splitkv")
+        seq = wls[0].seq_lens_host()
+        n, h = wls[0].num_nodes, wls[0].num_heads
+        flops = I.algorithmic_flops(seq, n, h)
+        med = pct(us, 0.5)
+        ksk = sum(sk) / len(sk)
+        out["random64-h64-ctx131072"] = {
+            "bound": "mfma", "calls": len(us),
+            "us_per_call": {"p10": round(pct(us, 0.1), 2), "p50": round(med, 2), "p90": round(pct(us, 0.9), 2)},
+            "tflops": round(flops / (med * 1e-6) / 1e12, 1),
+            "split_kernel_avg_us": round(ksk, 2),
+            "split_kernel_tflops": round(flops / (ksk * 1e-6) / 1e12, 1),
+            "peak_tflops": PEAK_BF16_TFLOPS,
+            "split_kernel_frac": round(flops / (ksk * 1e-6) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "gbps": round(I.algorithmic_bytes(seq, n, h) / (med * 1e-6) / 1e9, 1),
+            "flops_per_call": flops}
+        log("random64-h64-ctx131072: %.1f us/call, %.1f TFLOP/s (split kernel %.1f us, %.1f TFLOP/s)"
+            % (med, flops / (med * 1e-6) / 1e12, ksk, flops / (ksk * 1e-6) / 1e12))
+        del calls, wls, ws
+        torch.cuda.empty_cache()
+    if "c5" in names:
+        res = {}
+        outs = {}
+        base = I.config_workload(5, device="cuda", layout="scattered")
+        for layout in ("scattered", "runs64"):
+            log("building batch8-loguniform (%s)" % layout)
+            # identical logical values in both layouts: the runs-of-64 pool
+            # holds the scattered pool's rows at the new table's slots
+            wl = base if layout == "scattered" else I.relayout(
+                base, I.seed_for(5, 0, I.F_TABLE) + 1, "runs64")
+            c = M.prepare_workload(wl)
+            c.run()
+            torch.cuda.synchronize()
+            outs[layout] = (c.out.clone(), c.lse.clone())
+            us = time_each_call([c], args.steps, torch)
+            seq = wl.seq_lens_host()
+            b = I.algorithmic_bytes(seq, wl.num_nodes, wl.num_heads)
+            med = pct(us, 0.5)
+            res[layout] = {"us_per_call": {"p10": round(pct(us, 0.1), 2), "p50": round(med, 2),
+                                           "p90": round(pct(us, 0.9), 2)},
+                           "gbps": round(b / (med * 1e-6) / 1e9, 1),
+                           "pct_of_peak": round(100 * b / (med * 1e-6) / 1e9 / PEAK_GBPS, 2),
+                           "bytes_per_call": b, "seq_lens": [int(x) for x in seq]}
+            log("batch8-loguniform %s: %.2f us/call, %.0f GB/s" % (layout, med, b / (med * 1e-6) / 1e9))
+            del c, wl
+            torch.cuda.empty_cache()
+        del base
+        a, bb = outs["scattered"], outs["runs64"]
+        res["bitwise_equal"] = bool(torch.equal(a[0].view(torch.int16), bb[0].view(torch.int16))
+                                    and torch.equal(a[1].view(torch.int32), bb[1].view(torch.int32)))
+        out["batch8-loguniform"] = res
+    return out
 
 
 def sweep(args, torch, M, I):
@@ -233,6 +331,10 @@ def main() -> int:
     ap.add_argument("--sweep", default="65536,189440",
                     help="contexts of the 61-layer chain8 sweep ('' to skip)")
     ap.add_argument("--sweep-steps", type=int, default=5)
+    ap.add_argument("--configs", default="c4,c5",
+                    help="other configurations to time: c4 (64 nodes x 64 heads, ctx 131072), "
+                         "c5 (batch 8, mixed lengths, scattered and runs-of-64 layouts); '' for none")
+    ap.add_argument("--big-steps", type=int, default=20, help="timed calls of the c4 configuration")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="also run a plain copy of MIB MiB (for counter calibration)")
@@ -267,6 +369,7 @@ def main() -> int:
         % (sec * 1e6, value, hd["split_avg_ms"] * 1e3, hd["split_med_ms"] * 1e3, achieved))
 
     sw = sweep(args, torch, M, I)
+    oc = other_configs(args, torch, M, I)
     cpu = None if args.no_cpu_baseline else cpu_baseline(hd["wls"], hd["call_bytes"], I)
 
     wl = hd["wls"][0]
@@ -296,7 +399,9 @@ def main() -> int:
                      "frac": round(achieved / PEAK_GBPS, 4), "traffic": measured_traffic(),
                      "avg_launch_us": round(hd["split_avg_ms"] * 1e3, 3),
                      "bytes_per_launch": hd["split_bytes"]},
+        "call_us": hd["call_us"],
         "context_sweep": sw,
+        "other_configs": oc,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -46,7 +46,7 @@ size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 // The plan: enough slices per sequence that the batch's (sequence, row group)
 // pairs give about one workgroup per compute unit, each slice a whole number of
-// 32-key tiles and at most kMaxChunk keys.
+// 32-key tiles.
 mtv::Plan make_plan(const mtv_shape& s, int cus)
 {
     mtv::Plan p{};
@@ -59,10 +59,7 @@ mtv::Plan make_plan(const mtv_shape& s, int cus)
         splits = 1;
     if (splits > tiles)
         splits = tiles;
-    int64_t chunk_tiles = (tiles + splits - 1) / splits;
-    const int64_t max_tiles = mtv::kMaxChunk / mtv::kTileKeys;
-    if (chunk_tiles > max_tiles)
-        chunk_tiles = max_tiles;
+    const int64_t chunk_tiles = (tiles + splits - 1) / splits;
     splits = (tiles + chunk_tiles - 1) / chunk_tiles;
     p.splits = (int)splits;
     p.chunk = (int)(chunk_tiles * mtv::kTileKeys);

@@ -14,7 +14,6 @@ constexpr int kDv = 512;           // value width (the latent)
 constexpr int kRowBytes = kDqk * 2;
 constexpr int kTileKeys = 32;      // keys per LDS tile
 constexpr int kRowsPerGroup = 64;  // query rows per split workgroup (4 waves x 16)
-constexpr int kMaxChunk = 8192;    // keys per split (bounded by LDS index staging)
 
 // How one call is cut into workgroups. Depends only on host values.
 struct Plan {

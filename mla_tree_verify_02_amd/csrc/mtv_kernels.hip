@@ -31,7 +31,9 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
 constexpr int kWaves = 4;
-constexpr int kStages = 3;
+constexpr int kStages = 3;                                      // LDS tile buffers
+constexpr int kWinTiles = 128;                                  // tiles per staged index window
+constexpr int kWinKeys = kWinTiles * kTileKeys;                 // 4096 page indices per window
 constexpr int kChunks = kRowBytes / 16;                          // 72 x 16 B per row
 constexpr int kTileBytes = kTileKeys * kRowBytes;                // 36864
 constexpr int kKeysPerWave = kTileKeys / kWaves;                 // 8 rows loaded per wave
@@ -82,23 +84,37 @@ __device__ __forceinline__ int swz(int key)
     return key & 7;
 }
 
+// Items per XCD block: an eighth of the items, rounded up to whole slices when
+// a slice has at most 8 row groups.
+__host__ __device__ inline int xcd_block(int items, int row_groups)
+{
+    int per = (items + 7) / 8;
+    if (row_groups <= 8)
+        per = (per + row_groups - 1) / row_groups * row_groups;
+    return per;
+}
+
 __global__ __launch_bounds__(kThreads, 1) void split_kernel(Args a, int splits, int chunk,
                                                             int row_groups, float scale_log2)
 {
     __shared__ __attribute__((aligned(16))) char s_kv[kStages * kTileBytes];
-    __shared__ int s_idx[kMaxChunk];
+    __shared__ int s_idx[2][kWinKeys];  // page indices, two windows of 128 tiles
 
     // XCD-aware order: workgroups are dealt to the eight XCDs round-robin by
-    // id, so ids L and L + 8 share an XCD (and its L2). The row groups of one
-    // key slice get ids 8 apart and consecutive dispatch slots on one XCD,
-    // so all but the first read the slice's rows from that XCD's L2.
+    // id, so ids x, x + 8, x + 16, ... run on XCD x (and share its L2). The
+    // (slice, row group) items, slice-major, are cut into eight contiguous
+    // blocks, block x on XCD x, so the row groups of one slice run side by
+    // side on one XCD and all but the first read the slice's rows from its L2
+    // (with at most 8 row groups, blocks hold whole slices).
     const int L = blockIdx.x;
-    const int w8 = L >> 3;
-    const int grp = w8 % row_groups;
-    const int split = (w8 / row_groups) * 8 + (L & 7);
+    const int items = splits * row_groups;
+    const int per_xcd = xcd_block(items, row_groups);
+    const int item = (L & 7) * per_xcd + (L >> 3);
     const int b = blockIdx.y;
-    if (split >= splits)
-        return;  // padding of the slice count to a multiple of 8
+    if ((L >> 3) >= per_xcd || item >= items)
+        return;  // padding of the item count to a multiple of 8
+    const int split = item / row_groups;
+    const int grp = item - split * row_groups;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -115,17 +131,23 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(Args a, int splits, 
     const int nkeys = min(chunk, S - k0);
     const int ntiles = (nkeys + kTileKeys - 1) / kTileKeys;
 
-    // Stage the slice's page indices. Positions past the end reuse the last
-    // valid position's row (finite data, weight zero); indices are clamped so
-    // that no gather leaves the pool.
-    {
-        const int32_t* pt = a.page_table + (int64_t)b * a.max_kv;
-        const int maxslot = (int)(a.num_slots - 1);
-        for (int i = tid; i < ntiles * kTileKeys; i += kThreads) {
-            int v = pt[min(k0 + i, S - 1)];
-            s_idx[i] = v < 0 ? 0 : (v > maxslot ? maxslot : v);
+    // Stage the slice's page indices in windows of 128 tiles: window w (tiles
+    // 128w .. 128w+127) into s_idx[w % 2]. Positions past the end reuse the
+    // last valid position's row (finite data, weight zero); indices are
+    // clamped so that no gather leaves the pool. Window 0 is staged here; a
+    // slice longer than one window stages window w+1 halfway through window w.
+    const int32_t* pt = a.page_table + (int64_t)b * a.max_kv;
+    const int maxslot = (int)(a.num_slots - 1);
+    const int nwin = (ntiles + kWinTiles - 1) / kWinTiles;
+    auto stage = [&](int w) {
+        const int n = min(ntiles * kTileKeys - w * kWinKeys, kWinKeys);
+        int* dst = s_idx[w & 1];
+        for (int i = tid; i < n; i += kThreads) {
+            const int v = pt[min(k0 + w * kWinKeys + i, S - 1)];
+            dst[i] = v < 0 ? 0 : (v > maxslot ? maxslot : v);
         }
-    }
+    };
+    stage(0);
 
     // This lane's query row: fragments of Q as the B operand of S^T = K.Q^T.
     const int row = grp * kRowsPerGroup + wave * 16 + rl;
@@ -146,8 +168,6 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(Args a, int splits, 
     const uint32_t mw1 = W > 1 ? mrow[1] : 0u;
     const int tree0 = S - N;  // first key position holding a tree node
 
-    __syncthreads();  // indices staged
-
     const uint32_t lds0 = (uint32_t)(uintptr_t)(LDS_AS char*)s_kv;
     const char* kv = (const char*)a.kv;
 
@@ -163,10 +183,12 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(Args a, int splits, 
         gkl[j] = z / kChunks;
         gco[j] = ((z - gkl[j] * kChunks) ^ swz(gkl[j])) * 16;
     }
-    // Page indices of the rows this lane gathers for a tile, read from LDS one
-    // tile ahead of the gathers that use them.
+    // Page indices of the rows this lane gathers for a tile, read from the ring
+    // one tile ahead of the gathers that use them (nothing consumes them before
+    // then, so the LDS latency stays off the tile's path). Each wave reads only
+    // the words its own lanes loaded, so the vmcnt waits alone order them.
     auto load_idx = [&](int t, int* out) {
-        const int* tidx = s_idx + t * kTileKeys + wave * kKeysPerWave;
+        const int* tidx = &s_idx[(t / kWinTiles) & 1][(t % kWinTiles) * kTileKeys + wave * kKeysPerWave];
 #pragma unroll
         for (int j = 0; j < kLoadsPerWave; ++j)
             out[j] = tidx[gkl[j]];
@@ -211,9 +233,13 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(Args a, int splits, 
     float m_ref = -INFINITY;
     float l_run = 0.f;
 
-    // Q fragments and mask words must be in registers before the gathers start:
-    // past this point the only outstanding vector-memory operations are gathers.
+    // Q fragments and mask words must be in registers, and the first index
+    // window in LDS, before the gathers start: past this point the only
+    // outstanding vector-memory operations are this wave's gathers (and, on
+    // slices longer than a window, the reads of the next window, which the
+    // waits below only make stricter).
     wait_vmcnt<0>();
+    __syncthreads();  // index window 0 staged
     int idx_n[kLoadsPerWave];  // page indices of the next tile to gather
     load_idx(0, idx_n);
     issue(0, idx_n);
@@ -228,9 +254,13 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(Args a, int splits, 
     constexpr int kKReads = 2 * kKSteps;  // 36 per tile (two key blocks)
     constexpr int kVGroup = 4;            // column blocks per V-operand group
 
-    // Tile t's rows are in LDS once this wave's gathers have drained down to the
-    // later tiles' and every wave has passed the barrier; the barrier also frees
-    // the buffer of tile t-1 for the gathers of tile t+2.
+    // Tile t's rows are in LDS once at most the rows of tile t+1 remain
+    // outstanding and every wave has passed the barrier; the barrier also
+    // frees the buffer of tile t-1 for the gathers of tile t+2. Halfway
+    // through window w (step 128w + 64) the next window is staged into the
+    // other half of s_idx, whose last reader (tile 128w - 1) ran at step
+    // 128w - 4; later barriers publish it before its first reader (tile
+    // 128(w+1), at step 128(w+1) - 3).
     auto next_tile = [&](int t) {
         if (t + 1 < ntiles)
             wait_vmcnt<kLoadsPerWave>();
@@ -239,6 +269,8 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(Args a, int splits, 
         __syncthreads();
         if (t + 2 < ntiles)
             issue(t + 2, idx_n);
+        if (t % kWinTiles == kWinTiles / 2 && t / kWinTiles + 1 < nwin)
+            stage(t / kWinTiles + 1);
         if (t + 3 < ntiles)
             load_idx(t + 3, idx_n);
     };
@@ -418,25 +450,30 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(Args a, int splits, 
     }
 }
 
-// One workgroup per (sequence, 16-row block, 16-column block). Wave w merges
-// slices w, w+8, w+16, ... of its fragment lanes (running max and rescaled
-// sums), the eight waves then merge through LDS, and wave 0 writes the bf16
-// output (16 rows x 16 columns) and, for column block 0, the lse.
+// One workgroup of 8 waves per (sequence, 16-row block, group of 8/wpc
+// 16-column blocks): `wpc` waves share each column block (1, 2, 4 or 8, chosen
+// by the host from the slice count). A wave takes every wpc-th slice of its
+// column block, loads kCombineUnroll of them at once and folds them into its
+// running (max, sum, weighted sum) with one exp per slice against the round's
+// max. The waves of a column block then merge through LDS, and the first of
+// them writes the bf16 output (16 rows x 16 columns) and, for column block 0,
+// the lse.
 __global__ __launch_bounds__(kCombineThreads) void combine_kernel(Args a, int splits, int chunk,
-                                                                   int row_groups)
+                                                                   int row_groups, int wpc)
 {
     __shared__ float s_m[kCombineWaves][64];
     __shared__ float s_l[kCombineWaves][64];
     __shared__ f32x4 s_o[kCombineWaves][64];
 
-    const int cb = blockIdx.x;           // column block 0..31
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int cb = blockIdx.x * (kCombineWaves / wpc) + wave / wpc;  // column block 0..31
+    const int sub = wave % wpc;          // this wave's share of the slices
     const int rb = blockIdx.y;           // 16-row block within the sequence
     const int b = blockIdx.z;
     const int grp = rb >> 2;
     const int w = rb & 3;
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
     const int rl = lane & 15;
     const int N = a.nodes;
     const int R = N * a.heads;
@@ -449,19 +486,15 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(Args a, int sp
     const __bf16* pob = (const __bf16*)a.part_o + pbase * (size_t)(kRowsPerGroup * kPartRowElems) +
                         (size_t)w * (kColBlocks * 64 * 4) + (cb * 64 + lane) * 4;
 
-    // Each wave takes every kCombineWaves-th slice and loads kCombineUnroll of
-    // them at once (the whole slice set of a typical split in one round), then
-    // folds them into its running (max, sum, weighted sum) with one exp per
-    // slice against the round's max.
     float M = -INFINITY;
     float L = 0.f;
     f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int s0 = wave; s0 < nvalid; s0 += kCombineWaves * kCombineUnroll) {
+    for (int s0 = sub; s0 < nvalid; s0 += wpc * kCombineUnroll) {
         float2 ml[kCombineUnroll];
         f32x4 o[kCombineUnroll];
 #pragma unroll
         for (int u = 0; u < kCombineUnroll; ++u) {
-            const int s = s0 + u * kCombineWaves;
+            const int s = s0 + u * wpc;
             const bool in = s < nvalid;
             const size_t ss = in ? (size_t)s : 0;
             ml[u] = pml[ss * kRowsPerGroup];
@@ -496,20 +529,18 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(Args a, int sp
     s_l[wave][lane] = L;
     s_o[wave][lane] = acc;
     __syncthreads();
-    if (wave != 0)
+    if (sub != 0)
         return;
-    float Mt = s_m[0][lane];
-#pragma unroll
-    for (int k = 1; k < kCombineWaves; ++k)
-        Mt = fmaxf(Mt, s_m[k][lane]);
+    float Mt = s_m[wave][lane];
+    for (int k = 1; k < wpc; ++k)
+        Mt = fmaxf(Mt, s_m[wave + k][lane]);
     const float mref = (Mt == -INFINITY) ? 0.f : Mt;
     float Lt = 0.f;
     f32x4 ot = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int k = 0; k < kCombineWaves; ++k) {
-        const float c = exp2f(s_m[k][lane] - mref);  // 0 for waves that saw nothing
-        Lt += s_l[k][lane] * c;
-        ot += s_o[k][lane] * c;
+    for (int k = 0; k < wpc; ++k) {
+        const float c = exp2f(s_m[wave + k][lane] - mref);  // 0 for waves that saw nothing
+        Lt += s_l[wave + k][lane] * c;
+        ot += s_o[wave + k][lane] * c;
     }
     if (row >= R)
         return;
@@ -530,16 +561,21 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(Args a, int sp
 hipError_t launch_split(const Plan& p, const Args& a, hipStream_t stream)
 {
     const float scale_log2 = (float)((double)a.scale * 1.4426950408889634);
-    const int splits8 = (p.splits + 7) / 8 * 8;
-    hipLaunchKernelGGL(split_kernel, dim3(splits8 * p.row_groups, a.batch), dim3(kThreads), 0,
+    const int per_xcd = xcd_block(p.splits * p.row_groups, p.row_groups);
+    hipLaunchKernelGGL(split_kernel, dim3(8 * per_xcd, a.batch), dim3(kThreads), 0,
                        stream, a, p.splits, p.chunk, p.row_groups, scale_log2);
     return hipGetLastError();
 }
 
 hipError_t launch_combine(const Plan& p, const Args& a, hipStream_t stream)
 {
-    hipLaunchKernelGGL(combine_kernel, dim3(kColBlocks, p.row_groups * 4, a.batch), dim3(kCombineThreads),
-                       0, stream, a, p.splits, p.chunk, p.row_groups);
+    // waves per column block: enough that each loads at most kCombineUnroll
+    // slices per round, at most all eight
+    int wpc = 1;
+    while (wpc < kCombineWaves && wpc * kCombineUnroll < p.splits)
+        wpc *= 2;
+    hipLaunchKernelGGL(combine_kernel, dim3(kColBlocks * wpc / kCombineWaves, p.row_groups * 4, a.batch),
+                       dim3(kCombineThreads), 0, stream, a, p.splits, p.chunk, p.row_groups, wpc);
     return hipGetLastError();
 }
 

@@ -373,6 +373,27 @@ def config_workload(cid: int, *, device: str = "cpu", layer: int = 0, ctx: Optio
     raise ValueError(f"unknown config {cid}")
 
 
+def relayout(wl: Workload, table_seed: int, layout: str) -> Workload:
+    """The same logical inputs under another page table: every referenced KV row
+    moves to the slot the new table (`layout`, seeded by `table_seed`) gives its
+    position; Q, mask, lengths and scale are unchanged; unreferenced slots hold
+    NaN. Runs on the workload's device."""
+    other = make_workload(batch=wl.batch, num_nodes=wl.num_nodes, num_heads=wl.num_heads,
+                          prefix_lens=wl.prefix_lens, num_slots=wl.num_slots, tree="chain",
+                          layout=layout, table_seed=table_seed, config_id=0,
+                          mask=wl.np_mask(), device=str(wl.q.device),
+                          name=f"{wl.name}-{layout}")
+    other.q = wl.q.clone()
+    other.scale = wl.scale
+    old = wl.kv_pool.view(torch.int16)
+    new = torch.full_like(old, BF16_NAN_BITS)
+    t_old, t_new = wl.page_table.long(), other.page_table.long()
+    for b, s in enumerate(wl.seq_lens_host()):
+        new[t_new[b, :s]] = old[t_old[b, :s]]
+    other.kv_pool = new.view(torch.bfloat16)
+    return other
+
+
 def algorithmic_bytes(seq_lens: Sequence[int], num_nodes: int, num_heads: int) -> int:
     """Bytes a call must move at minimum: every referenced 1152-byte KV row once
     and its 4-byte page index, Q in, out and lse out, and the mask."""

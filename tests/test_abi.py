@@ -59,10 +59,15 @@ def test_workspace_size_validates_shape(shape, ok):
 ])
 def test_plan_covers_every_key(b, n, h, max_kv, cus):
     p = M.plan_query(M.make_shape(b, n, h, max_kv, 1 << 20), cus)
-    assert p["chunk"] % 32 == 0 and 32 <= p["chunk"] <= 8192
+    tiles = (max_kv + 31) // 32
+    assert p["chunk"] % 32 == 0 and 32 <= p["chunk"] <= 32 * tiles
     assert p["splits"] * p["chunk"] >= max_kv
     assert (p["splits"] - 1) * p["chunk"] < max_kv
     assert p["row_groups"] == (n * h + 63) // 64
+    # about one workgroup per compute unit whenever there is that much work
+    # (rounding the slices to whole tiles can lose up to half of it)
+    pairs = b * p["row_groups"]
+    assert pairs * p["splits"] >= min(cus, pairs * tiles) // 2
 
 
 def _call(shape, ptrs=None, ws_bytes=1 << 30, scale=0.07):

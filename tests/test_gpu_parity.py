@@ -111,26 +111,12 @@ def test_empty_visible_set(oracle_mod):
 
 # ---------------------------------------------------- bit-exact index / mask handling
 
-def relayout_gpu(wl, table_seed, layout):
-    other = I.make_workload(batch=wl.batch, num_nodes=wl.num_nodes, num_heads=wl.num_heads,
-                            prefix_lens=wl.prefix_lens, num_slots=wl.num_slots, tree="chain",
-                            layout=layout, table_seed=table_seed, config_id=103,
-                            mask=wl.np_mask(), device="cuda")
-    other.q = wl.q.clone()
-    kv_new = torch.full_like(wl.kv_pool.view(torch.int16), I.BF16_NAN_BITS)
-    t_old, t_new = wl.page_table.long(), other.page_table.long()
-    for b, S in enumerate(wl.seq_lens_host()):
-        kv_new[t_new[b, :S]] = wl.kv_pool.view(torch.int16)[t_old[b, :S]]
-    other.kv_pool = kv_new.view(torch.bfloat16)
-    return other
-
-
 def test_layout_invariance_bitwise():
     wl = I.make_workload(batch=3, num_nodes=8, num_heads=8, prefix_lens=[5000, 77, 12345],
                          num_slots=65536, tree="random", max_depth=5, config_id=104, device="cuda")
     ref = run_gpu(wl)
     for seed, layout in [(11, "scattered"), (12, "runs64")]:
-        got = run_gpu(relayout_gpu(wl, seed, layout))
+        got = run_gpu(I.relayout(wl, seed, layout))
         assert np.array_equal(got[0], ref[0])
         assert np.array_equal(got[1].view(np.uint32), ref[1].view(np.uint32))
 
@@ -192,7 +178,7 @@ def test_random64_h64_ctx131072(oracle_mod):
 def test_batch8_both_layouts(oracle_mod):
     a = I.config_workload(5, device="cuda", layout="scattered")
     g_a = compare(a, oracle_mod, rows=sample_rows(a, 40, seed=5), label="batch8 scattered")
-    b = relayout_gpu(a, I.seed_for(5, 0, I.F_TABLE) + 1, "runs64")
+    b = I.relayout(a, I.seed_for(5, 0, I.F_TABLE) + 1, "runs64")
     ga = run_gpu(a)
     gb = run_gpu(b)
     assert np.array_equal(ga[0], gb[0]) and np.array_equal(ga[1], gb[1])

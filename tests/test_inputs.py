@@ -78,3 +78,20 @@ def test_config_shapes():
     assert tuple(wl.q.shape) == (1, 8, 8, 576) and wl.max_kv == 1032 and wl.num_slots == 4096
     pre = I.log_uniform_prefixes(8, 1024, 131072, I.seed_for(5, 0, I.F_LENS))
     assert all(1024 <= p <= 131072 for p in pre)
+
+
+def test_relayout_moves_every_referenced_row_and_nothing_else():
+    wl = I.make_workload(batch=2, num_nodes=8, num_heads=2, prefix_lens=[300, 77],
+                         num_slots=1024, tree="binary", config_id=7)
+    for seed, layout in [(5, "scattered"), (6, "runs64")]:
+        other = I.relayout(wl, seed, layout)
+        old = wl.kv_pool.view(torch.int16)
+        new = other.kv_pool.view(torch.int16)
+        referenced = torch.zeros(wl.num_slots, dtype=torch.bool)
+        for b, s in enumerate(wl.seq_lens_host()):
+            t_old, t_new = wl.page_table[b, :s].long(), other.page_table[b, :s].long()
+            assert torch.equal(new[t_new], old[t_old])
+            referenced[t_new] = True
+        assert bool((new[~referenced] == I.BF16_NAN_BITS).all())
+        assert torch.equal(other.q, wl.q) and np.array_equal(other.np_mask(), wl.np_mask())
+        assert other.seq_lens_host() == wl.seq_lens_host() and other.scale == wl.scale
