@@ -163,8 +163,9 @@ def headline(args, torch, M, I):
 
 
 def other_configs(args, torch, M, I):
-    """The all-heads configuration (64 nodes x 64 heads, MFMA-bound) and the
-    batch-8 mixed-length configuration in both page layouts."""
+    """The all-heads configuration (64 nodes x 64 heads, MFMA-bound), the
+    batch-8 mixed-length configuration in both page layouts, and the tree-mask
+    build from parent arrays."""
     out = {}
     names = [c.strip() for c in args.configs.split(",") if c.strip()]
     if "c4" in names:
@@ -230,6 +231,25 @@ def other_configs(args, torch, M, I):
         res["bitwise_equal"] = bool(torch.equal(a[0].view(torch.int16), bb[0].view(torch.int16))
                                     and torch.equal(a[1].view(torch.int32), bb[1].view(torch.int32)))
         out["batch8-loguniform"] = res
+    if "mask" in names:
+        # the tree-mask build before the verify step (parent array -> bitmask)
+        import numpy as np
+        res = {}
+        for b, n in ((1, 64), (8, 8), (4096, 64)):
+            parents = torch.from_numpy(np.stack([I.random_parents(n, 8, 70_000 + s) for s in range(b)])
+                                       .astype(np.int32)).cuda()
+            mask = M.tree_mask_build(parents)
+
+            class _Call:
+                def run(self):
+                    M.tree_mask_build(parents, out=mask)
+            us = time_each_call([_Call()], 200, torch)
+            res["b%d_n%d" % (b, n)] = {"us_per_call": {"p10": round(pct(us, 0.1), 2),
+                                                       "p50": round(pct(us, 0.5), 2),
+                                                       "p90": round(pct(us, 0.9), 2)},
+                                       "nodes_per_s": round(b * n / (pct(us, 0.5) * 1e-6), 1)}
+            log("tree mask build B=%d N=%d: %.2f us/call" % (b, n, pct(us, 0.5)))
+        out["tree_mask_build"] = res
     return out
 
 
@@ -314,8 +334,20 @@ def cpu_baseline(wls, call_bytes, I):
                     break
     except OSError:
         pass
+    # the tree-mask oracle on the shapes the mask-build line times
+    from oracle import tree_mask as TM
+    import numpy as np
+    mask_us = {}
+    for b, n in ((1, 64), (8, 8), (4096, 64)):
+        parents = np.stack([I.random_parents(n, 8, 70_000 + s) for s in range(b)]).astype(np.int32)
+        reps = 20 if b < 100 else 1
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            TM.tree_mask(parents)
+        mask_us["b%d_n%d" % (b, n)] = round((time.perf_counter() - t0) / reps * 1e6, 1)
     rows = wls[0].batch * wls[0].num_nodes * wls[0].num_heads
     return {"value": round(calls * call_bytes / total / 1e9, 4), "unit": "GB/s",
+            "tree_mask_build_us": mask_us,
             "cores": threads, "kind": "oracle", "seconds": round(total, 3),
             "cpu_model": model,
             "sample": "%d full calls (all %d rows each) of the binary16-ctx65536 workload, "
@@ -331,9 +363,10 @@ def main() -> int:
     ap.add_argument("--sweep", default="65536,189440",
                     help="contexts of the 61-layer chain8 sweep ('' to skip)")
     ap.add_argument("--sweep-steps", type=int, default=5)
-    ap.add_argument("--configs", default="c4,c5",
+    ap.add_argument("--configs", default="c4,c5,mask",
                     help="other configurations to time: c4 (64 nodes x 64 heads, ctx 131072), "
-                         "c5 (batch 8, mixed lengths, scattered and runs-of-64 layouts); '' for none")
+                         "c5 (batch 8, mixed lengths, scattered and runs-of-64 layouts), "
+                         "mask (the tree-mask build from parent arrays); '' for none")
     ap.add_argument("--big-steps", type=int, default=20, help="timed calls of the c4 configuration")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",

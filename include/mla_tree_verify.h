@@ -164,6 +164,31 @@ int mla_tree_verify_combine(const mtv_shape* shape,
                             size_t workspace_bytes,
                             hipStream_t stream);
 
+/*
+ * Enqueue, on `stream`, the build of tree_mask from the draft tree's parent
+ * array: node i may attend tree node j iff j == i or j is an ancestor of i.
+ * This is the visibility the verify attention applies to the tree block ("The
+ * GPU That Wasn't There", The Native Engine Thesis; "The Moment of Certainty",
+ * The Path Forward: From Diagnosis to Solution), built on the device instead
+ * of the host ("The GPU That Wasn't There", Assumptions and Their Validity,
+ * which times the host build).
+ *
+ * Device pointers (caller-owned, 4-byte aligned):
+ *   parents    int32 [B][N]   parent of node i, in [-1, i): -1 marks a root
+ *                             (forests are allowed). Any other value is read as
+ *                             -1, so a malformed tree still yields a valid mask.
+ *   tree_mask  uint32 [B][N][W], W = ceil(N/32), the layout mla_tree_verify
+ *                             reads; written in full (bits j >= N are zero).
+ * batch in [1, MTV_MAX_BATCH], num_nodes in [1, MTV_MAX_NODES].
+ * Returns MTV_OK or MTV_ERR_NULL / MTV_ERR_SHAPE / MTV_ERR_ALIGN / MTV_ERR_HIP.
+ * Never allocates or synchronises; the call may be captured into a HIP graph.
+ */
+int mla_tree_mask_build(int32_t batch,
+                        int32_t num_nodes,
+                        const int32_t* parents,
+                        uint32_t* tree_mask,
+                        hipStream_t stream);
+
 /* Static, human-readable text for a status code. */
 const char* mtv_status_string(int status);
 

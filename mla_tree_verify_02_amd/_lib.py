@@ -19,7 +19,8 @@ MTV_OK = 0
 STATUS_NAMES = {0: "MTV_OK", -1: "MTV_ERR_NULL", -2: "MTV_ERR_SHAPE", -3: "MTV_ERR_ALIGN",
                 -4: "MTV_ERR_WORKSPACE", -5: "MTV_ERR_HIP"}
 EXPORTED = ("mla_tree_verify", "mla_tree_verify_workspace_size", "mtv_status_string",
-            "mtv_plan_query", "mla_tree_verify_splitkv", "mla_tree_verify_combine")
+            "mtv_plan_query", "mla_tree_verify_splitkv", "mla_tree_verify_combine",
+            "mla_tree_mask_build")
 
 
 class MtvShape(ctypes.Structure):
@@ -65,6 +66,8 @@ def load(path: Optional[str] = None):
     lib.mtv_plan_query.restype = ctypes.c_int
     IP = ctypes.POINTER(ctypes.c_int)
     lib.mtv_plan_query.argtypes = [SP, ctypes.c_int, IP, IP, IP]
+    lib.mla_tree_mask_build.restype = ctypes.c_int
+    lib.mla_tree_mask_build.argtypes = [ctypes.c_int32, ctypes.c_int32, VP, VP, VP]
     if path is None:
         _lib = lib
     return lib
@@ -168,6 +171,40 @@ def mla_tree_verify(q: torch.Tensor, kv_pool: torch.Tensor, page_table: torch.Te
     if rc != MTV_OK:
         raise MtvError(rc, status_string(rc))
     return out, lse
+
+
+def tree_mask_build(parents: torch.Tensor, out: Optional[torch.Tensor] = None, stream=None):
+    """Ancestor-or-self visibility bitmask from a parent array, built by the
+    library's kernel.
+
+    parents int32 [B, N] on a GPU (parent of node i in [-1, i), -1 for roots;
+    other values are read as -1). Returns int32 bit patterns [B, N, ceil(N/32)]
+    in the layout mla_tree_verify takes as tree_mask.
+    """
+    if parents.dim() != 2:
+        raise ValueError("parents must be [B, N]")
+    B, N = parents.shape
+    dev = parents.device
+    if dev.type != "cuda":
+        raise ValueError("parents must be on a GPU")
+    _check(parents, "parents", torch.int32, (B, N), dev)
+    W = (N + 31) // 32
+    if out is None:
+        out = torch.empty((B, N, W), dtype=torch.int32, device=dev)
+    else:
+        if out.dtype not in (torch.int32, getattr(torch, "uint32", torch.int32)):
+            raise TypeError("out must hold 32-bit words")
+        _check(out, "out", out.dtype, (B, N, W), dev)
+    lib = load()
+    with torch.cuda.device(dev):
+        if stream is None:
+            stream = torch.cuda.current_stream(dev)
+        handle = ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+        rc = lib.mla_tree_mask_build(ctypes.c_int32(B), ctypes.c_int32(N), _ptr(parents), _ptr(out),
+                                     handle)
+    if rc != MTV_OK:
+        raise MtvError(rc, status_string(rc))
+    return out
 
 
 def verify_workload(wl, **kw):

@@ -10,7 +10,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB_NAME = "libmla_tree_verify.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
-SOURCES = [os.path.join(CSRC, "mtv_api.cpp"), os.path.join(CSRC, "mtv_kernels.hip")]
+SOURCES = [os.path.join(CSRC, "mtv_api.cpp"), os.path.join(CSRC, "mtv_kernels.hip"),
+           os.path.join(CSRC, "mtv_tree.hip")]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

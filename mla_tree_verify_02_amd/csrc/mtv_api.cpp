@@ -191,6 +191,20 @@ int mla_tree_verify_combine(const mtv_shape* shape, const int32_t* seq_lens, voi
                workspace, workspace_bytes, stream);
 }
 
+int mla_tree_mask_build(int32_t batch, int32_t num_nodes, const int32_t* parents,
+                        uint32_t* tree_mask, hipStream_t stream)
+{
+    if (!parents || !tree_mask)
+        return MTV_ERR_NULL;
+    if (batch < 1 || batch > MTV_MAX_BATCH || num_nodes < 1 || num_nodes > MTV_MAX_NODES)
+        return MTV_ERR_SHAPE;
+    if (!aligned(parents, 4) || !aligned(tree_mask, 4))
+        return MTV_ERR_ALIGN;
+    if (mtv::launch_tree_mask(batch, num_nodes, parents, tree_mask, stream) != hipSuccess)
+        return MTV_ERR_HIP;
+    return MTV_OK;
+}
+
 const char* mtv_status_string(int status)
 {
     switch (status) {

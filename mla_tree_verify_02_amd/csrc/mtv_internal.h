@@ -41,5 +41,7 @@ struct Args {
 
 hipError_t launch_split(const Plan& plan, const Args& a, hipStream_t stream);
 hipError_t launch_combine(const Plan& plan, const Args& a, hipStream_t stream);
+hipError_t launch_tree_mask(int batch, int nodes, const int32_t* parents, uint32_t* mask,
+                            hipStream_t stream);
 
 }  // namespace mtv

@@ -116,3 +116,15 @@ def test_python_binding_rejects_host_tensors():
 def test_missing_library_fails_loudly(tmp_path):
     with pytest.raises(FileNotFoundError):
         _lib.load(str(tmp_path / "nope.so"))
+
+
+def test_tree_mask_build_rejects_bad_arguments():
+    lib = M.load()
+    V = ctypes.c_void_p
+    good = 1 << 20
+    assert lib.mla_tree_mask_build(1, 8, None, V(good), None) == -1
+    assert lib.mla_tree_mask_build(1, 8, V(good), None, None) == -1
+    for b, n in [(0, 8), (1, 0), (1, 65), (70000, 8)]:
+        assert lib.mla_tree_mask_build(b, n, V(good), V(good), None) == -2
+    assert lib.mla_tree_mask_build(1, 8, V(good + 2), V(good), None) == -3
+    assert lib.mla_tree_mask_build(1, 8, V(good), V(good + 1), None) == -3
