@@ -250,7 +250,88 @@ def other_configs(args, torch, M, I):
                                        "nodes_per_s": round(b * n / (pct(us, 0.5) * 1e-6), 1)}
             log("tree mask build B=%d N=%d: %.2f us/call" % (b, n, pct(us, 0.5)))
         out["tree_mask_build"] = res
+    if "kv" in names:
+        out["kv_moves"] = kv_moves(torch, M, I)
     return out
+
+
+def kv_moves(torch, M, I):
+    """Tier-0 moves after a verify step: a whole sequence gathered from
+    scattered slots into a fresh contiguous run (HBM-bound copy, reported
+    against 8 TB/s), and the accepted-path commit. The page table is restored
+    before each call, outside the timed bracket; 4 source/destination sets
+    rotate so that the Infinity Cache cannot serve repeats."""
+    import numpy as np
+    res = {}
+    stream = torch.cuda.current_stream()
+    for S in (65536, 189448):
+        R = 4
+        P = 2 * R * S
+        pool = torch.empty((P, I.D_QK), dtype=torch.bfloat16, device="cuda")
+        pool.view(torch.int16).random_()
+        tables, bases = [], []
+        for r in range(R):
+            g = torch.Generator().manual_seed(4242 + r)
+            src = (2 * r * S + torch.randperm(S, generator=g)).to(torch.int32)
+            tables.append(src.view(1, S).cuda())
+            bases.append(torch.tensor([2 * r * S + S], dtype=torch.int32, device="cuda"))
+        seq = torch.tensor([S], dtype=torch.int32, device="cuda")
+        work = torch.empty((1, S), dtype=torch.int32, device="cuda")
+        ev = []
+        for k in range(8 + 40):
+            r = k % R
+            work.copy_(tables[r])
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            M.kv_defrag(pool, work, seq, bases[r])
+            e1.record(stream)
+            if k >= 8:
+                ev.append((e0, e1))
+        torch.cuda.synchronize()
+        us = sorted(a.elapsed_time(b) * 1e3 for a, b in ev)
+        nbytes = S * (2 * I.ROW_BYTES + 8) + 8
+        med = pct(us, 0.5)
+        res["defrag_s%d" % S] = {"us_per_call": {"p10": round(pct(us, 0.1), 2), "p50": round(med, 2),
+                                                 "p90": round(pct(us, 0.9), 2)},
+                                 "bytes_per_call": nbytes, "gbps": round(nbytes / (med * 1e-6) / 1e9, 1),
+                                 "frac_of_8tbs": round(nbytes / (med * 1e-6) / 1e9 / PEAK_GBPS, 4)}
+        log("defrag of %d rows: %.2f us, %.0f GB/s" % (S, med, nbytes / (med * 1e-6) / 1e9))
+        del pool, tables, work
+        torch.cuda.empty_cache()
+    # accepted-path commit: heap-binary 16-node tree, path 0-1-3-7-15 (L = 5);
+    # and batch 8 of 8-node chains, 4 accepted each
+    for B, N, path in ((1, 16, [0, 1, 3, 7, 15]), (8, 8, [0, 1, 2, 3])):
+        S0 = 4096
+        P = 2 * B * S0
+        pool = torch.empty((P, I.D_QK), dtype=torch.bfloat16, device="cuda")
+        pool.view(torch.int16).random_()
+        g = torch.Generator().manual_seed(99)
+        table0 = torch.randperm(B * S0, generator=g).to(torch.int32).view(B, S0).cuda()
+        seq = torch.full((B,), S0, dtype=torch.int32, device="cuda")
+        alen = torch.full((B,), len(path), dtype=torch.int32, device="cuda")
+        apath = torch.zeros((B, N), dtype=torch.int32)
+        apath[:, :len(path)] = torch.tensor(path, dtype=torch.int32)
+        apath = apath.cuda()
+        base = (B * S0 + S0 * torch.arange(B, dtype=torch.int32)).cuda()
+        work = table0.clone()
+        ev = []
+        for k in range(20 + 200):
+            work.copy_(table0)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            M.kv_commit(pool, work, seq, N, alen, apath, base)
+            e1.record(stream)
+            if k >= 20:
+                ev.append((e0, e1))
+        torch.cuda.synchronize()
+        us = sorted(a.elapsed_time(b) * 1e3 for a, b in ev)
+        res["commit_b%d_n%d_l%d" % (B, N, len(path))] = {
+            "us_per_call": {"p10": round(pct(us, 0.1), 2), "p50": round(pct(us, 0.5), 2),
+                            "p90": round(pct(us, 0.9), 2)},
+            "rows_moved": B * len(path)}
+        log("commit B=%d N=%d L=%d: %.2f us/call" % (B, N, len(path), pct(us, 0.5)))
+        del pool
+    return res
 
 
 def sweep(args, torch, M, I):
@@ -345,9 +426,21 @@ def cpu_baseline(wls, call_bytes, I):
         for _ in range(reps):
             TM.tree_mask(parents)
         mask_us["b%d_n%d" % (b, n)] = round((time.perf_counter() - t0) / reps * 1e6, 1)
+    # the KV-move oracle: one accepted-path commit and a 65,536-row defrag
+    from oracle import kv_move as KM
+    pool = np.random.default_rng(1).integers(0, 1 << 16, size=(2 * 65536, 576), dtype=np.uint16)
+    table = np.random.default_rng(2).permutation(65536).astype(np.int32).reshape(1, 65536)
+    t0 = time.perf_counter()
+    KM.kv_commit(pool, table, [65536], 16, [5], [[0, 1, 3, 7, 15] + [0] * 11], [65536])
+    commit_us = (time.perf_counter() - t0) * 1e6
+    t0 = time.perf_counter()
+    KM.kv_defrag(pool, table, [65536], [65536])
+    defrag_us = (time.perf_counter() - t0) * 1e6
     rows = wls[0].batch * wls[0].num_nodes * wls[0].num_heads
     return {"value": round(calls * call_bytes / total / 1e9, 4), "unit": "GB/s",
             "tree_mask_build_us": mask_us,
+            "kv_commit_b1_n16_l5_us": round(commit_us, 1),
+            "kv_defrag_s65536_us": round(defrag_us, 1),
             "cores": threads, "kind": "oracle", "seconds": round(total, 3),
             "cpu_model": model,
             "sample": "%d full calls (all %d rows each) of the binary16-ctx65536 workload, "
@@ -363,10 +456,11 @@ def main() -> int:
     ap.add_argument("--sweep", default="65536,189440",
                     help="contexts of the 61-layer chain8 sweep ('' to skip)")
     ap.add_argument("--sweep-steps", type=int, default=5)
-    ap.add_argument("--configs", default="c4,c5,mask",
+    ap.add_argument("--configs", default="c4,c5,mask,kv",
                     help="other configurations to time: c4 (64 nodes x 64 heads, ctx 131072), "
                          "c5 (batch 8, mixed lengths, scattered and runs-of-64 layouts), "
-                         "mask (the tree-mask build from parent arrays); '' for none")
+                         "mask (the tree-mask build from parent arrays), "
+                         "kv (Tier-0 defrag and accepted-path commit); '' for none")
     ap.add_argument("--big-steps", type=int, default=20, help="timed calls of the c4 configuration")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",

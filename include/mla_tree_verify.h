@@ -189,6 +189,68 @@ int mla_tree_mask_build(int32_t batch,
                         uint32_t* tree_mask,
                         hipStream_t stream);
 
+/*
+ * Tier-0 commit of an accepted tree path, enqueued on `stream`: the accepted
+ * nodes' latent rows move from their scattered tree-block slots into the
+ * request's contiguous run of slots, and the page table follows them. The
+ * pages keep per-request KV contiguous in the pool this way ("The Moment of
+ * Reckoning: A User's Challenge That Reshaped a Long-Context Inference
+ * Investigation", Output Knowledge Created by This Message); the tree block is
+ * what is scattered ("The Moment of Certainty", The User Provides the Final
+ * Piece).
+ *
+ * For each sequence b, with S_b = seq_lens[b] clamped to [N, max_kv],
+ * t0 = S_b - N (the first tree position), L = accept_len[b] clamped to [0, N]
+ * and k < L:
+ *   node n_k = accept_path[b][k] (clamped to [0, N)),
+ *   source slot = page_table[b][t0 + n_k], destination = region_base[b] + t0 + k;
+ *   the source row is copied to the destination and page_table[b][t0 + k] is
+ *   set to the destination. Every source row of a sequence is read before any
+ *   of its destinations is written, so the destinations may overlap that
+ *   sequence's own tree-block slots.
+ * Device pointers (caller-owned): kv_pool bf16 [num_slots][576] (16-byte
+ * aligned; rows are moved in place), page_table int32 [B][max_kv] (updated),
+ * seq_lens int32 [B], accept_len int32 [B], accept_path int32 [B][N] (the path
+ * in commit order, e.g. root first), region_base int32 [B] (slot of position
+ * 0 of the request's run); all 4-byte aligned. Different sequences' reads and
+ * writes must not overlap one another. Slots are clamped to the pool on read;
+ * a destination outside the pool is skipped and its table entry kept. The
+ * caller advances seq_lens to t0 + L for the next step.
+ * Returns MTV_OK or MTV_ERR_NULL / MTV_ERR_SHAPE / MTV_ERR_ALIGN / MTV_ERR_HIP.
+ */
+int mla_kv_commit(int32_t batch,
+                  int32_t num_nodes,
+                  int32_t max_kv,
+                  int64_t num_slots,
+                  void* kv_pool,
+                  int32_t* page_table,
+                  const int32_t* seq_lens,
+                  const int32_t* accept_len,
+                  const int32_t* accept_path,
+                  const int32_t* region_base,
+                  hipStream_t stream);
+
+/*
+ * Tier-0 defragmentation of whole sequences (same pages as mla_kv_commit),
+ * enqueued on `stream`: the rows of positions [0, S_b) of sequence b, S_b =
+ * seq_lens[b] clamped to [0, max_kv], are copied from their page-table slots to
+ * region_base[b] + p, and page_table[b][p] is set to region_base[b] + p. The
+ * destination runs must not overlap any source row or each other (for
+ * instance, a freshly allocated region); otherwise the result is unspecified
+ * (never out of bounds: reads are clamped to the pool, destinations outside it
+ * skipped). Pointers as for mla_kv_commit. Two launches: the copy, then the
+ * table rewrite.
+ * Returns MTV_OK or MTV_ERR_NULL / MTV_ERR_SHAPE / MTV_ERR_ALIGN / MTV_ERR_HIP.
+ */
+int mla_kv_defrag(int32_t batch,
+                  int32_t max_kv,
+                  int64_t num_slots,
+                  void* kv_pool,
+                  int32_t* page_table,
+                  const int32_t* seq_lens,
+                  const int32_t* region_base,
+                  hipStream_t stream);
+
 /* Static, human-readable text for a status code. */
 const char* mtv_status_string(int status);
 

@@ -20,7 +20,7 @@ STATUS_NAMES = {0: "MTV_OK", -1: "MTV_ERR_NULL", -2: "MTV_ERR_SHAPE", -3: "MTV_E
                 -4: "MTV_ERR_WORKSPACE", -5: "MTV_ERR_HIP"}
 EXPORTED = ("mla_tree_verify", "mla_tree_verify_workspace_size", "mtv_status_string",
             "mtv_plan_query", "mla_tree_verify_splitkv", "mla_tree_verify_combine",
-            "mla_tree_mask_build")
+            "mla_tree_mask_build", "mla_kv_commit", "mla_kv_defrag")
 
 
 class MtvShape(ctypes.Structure):
@@ -68,6 +68,11 @@ def load(path: Optional[str] = None):
     lib.mtv_plan_query.argtypes = [SP, ctypes.c_int, IP, IP, IP]
     lib.mla_tree_mask_build.restype = ctypes.c_int
     lib.mla_tree_mask_build.argtypes = [ctypes.c_int32, ctypes.c_int32, VP, VP, VP]
+    I32, I64 = ctypes.c_int32, ctypes.c_int64
+    lib.mla_kv_commit.restype = ctypes.c_int
+    lib.mla_kv_commit.argtypes = [I32, I32, I32, I64, VP, VP, VP, VP, VP, VP, VP]
+    lib.mla_kv_defrag.restype = ctypes.c_int
+    lib.mla_kv_defrag.argtypes = [I32, I32, I64, VP, VP, VP, VP, VP]
     if path is None:
         _lib = lib
     return lib
@@ -205,6 +210,63 @@ def tree_mask_build(parents: torch.Tensor, out: Optional[torch.Tensor] = None, s
     if rc != MTV_OK:
         raise MtvError(rc, status_string(rc))
     return out
+
+
+def _stream_handle(dev, stream):
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def kv_commit(kv_pool: torch.Tensor, page_table: torch.Tensor, seq_lens: torch.Tensor,
+              num_nodes: int, accept_len: torch.Tensor, accept_path: torch.Tensor,
+              region_base: torch.Tensor, stream=None) -> None:
+    """Move each sequence's accepted tree nodes into its contiguous run of
+    slots and update the page table in place (see mla_kv_commit)."""
+    dev = kv_pool.device
+    if dev.type != "cuda":
+        raise ValueError("kv_pool must be on a GPU")
+    if kv_pool.dim() != 2 or page_table.dim() != 2:
+        raise ValueError("kv_pool must be [num_slots, 576] and page_table [B, max_kv]")
+    P = kv_pool.shape[0]
+    B, max_kv = page_table.shape
+    N = int(num_nodes)
+    _check(kv_pool, "kv_pool", torch.bfloat16, (P, 576), dev)
+    _check(page_table, "page_table", torch.int32, (B, max_kv), dev)
+    _check(seq_lens, "seq_lens", torch.int32, (B,), dev)
+    _check(accept_len, "accept_len", torch.int32, (B,), dev)
+    _check(accept_path, "accept_path", torch.int32, (B, N), dev)
+    _check(region_base, "region_base", torch.int32, (B,), dev)
+    lib = load()
+    with torch.cuda.device(dev):
+        rc = lib.mla_kv_commit(B, N, max_kv, P, _ptr(kv_pool), _ptr(page_table), _ptr(seq_lens),
+                               _ptr(accept_len), _ptr(accept_path), _ptr(region_base),
+                               _stream_handle(dev, stream))
+    if rc != MTV_OK:
+        raise MtvError(rc, status_string(rc))
+
+
+def kv_defrag(kv_pool: torch.Tensor, page_table: torch.Tensor, seq_lens: torch.Tensor,
+              region_base: torch.Tensor, stream=None) -> None:
+    """Move every sequence's rows to region_base[b] + position and rewrite the
+    page table in place (see mla_kv_defrag)."""
+    dev = kv_pool.device
+    if dev.type != "cuda":
+        raise ValueError("kv_pool must be on a GPU")
+    if kv_pool.dim() != 2 or page_table.dim() != 2:
+        raise ValueError("kv_pool must be [num_slots, 576] and page_table [B, max_kv]")
+    P = kv_pool.shape[0]
+    B, max_kv = page_table.shape
+    _check(kv_pool, "kv_pool", torch.bfloat16, (P, 576), dev)
+    _check(page_table, "page_table", torch.int32, (B, max_kv), dev)
+    _check(seq_lens, "seq_lens", torch.int32, (B,), dev)
+    _check(region_base, "region_base", torch.int32, (B,), dev)
+    lib = load()
+    with torch.cuda.device(dev):
+        rc = lib.mla_kv_defrag(B, max_kv, P, _ptr(kv_pool), _ptr(page_table), _ptr(seq_lens),
+                               _ptr(region_base), _stream_handle(dev, stream))
+    if rc != MTV_OK:
+        raise MtvError(rc, status_string(rc))
 
 
 def verify_workload(wl, **kw):

@@ -205,6 +205,48 @@ int mla_tree_mask_build(int32_t batch, int32_t num_nodes, const int32_t* parents
     return MTV_OK;
 }
 
+int mla_kv_commit(int32_t batch, int32_t num_nodes, int32_t max_kv, int64_t num_slots,
+                  void* kv_pool, int32_t* page_table, const int32_t* seq_lens,
+                  const int32_t* accept_len, const int32_t* accept_path,
+                  const int32_t* region_base, hipStream_t stream)
+{
+    if (!kv_pool || !page_table || !seq_lens || !accept_len || !accept_path || !region_base)
+        return MTV_ERR_NULL;
+    if (batch < 1 || batch > MTV_MAX_BATCH || num_nodes < 1 || num_nodes > MTV_MAX_NODES ||
+        max_kv < num_nodes || max_kv > MTV_MAX_KV || num_slots < 1 || num_slots > INT32_MAX)
+        return MTV_ERR_SHAPE;
+    if (!aligned(kv_pool, 16) || !aligned(page_table, 4) || !aligned(seq_lens, 4) ||
+        !aligned(accept_len, 4) || !aligned(accept_path, 4) || !aligned(region_base, 4))
+        return MTV_ERR_ALIGN;
+    mtv::KvArgs a{batch, num_nodes, max_kv, num_slots, kv_pool, page_table, seq_lens,
+                  accept_len, accept_path, region_base};
+    if (mtv::launch_kv_commit(a, stream) != hipSuccess)
+        return MTV_ERR_HIP;
+    return MTV_OK;
+}
+
+int mla_kv_defrag(int32_t batch, int32_t max_kv, int64_t num_slots, void* kv_pool,
+                  int32_t* page_table, const int32_t* seq_lens, const int32_t* region_base,
+                  hipStream_t stream)
+{
+    if (!kv_pool || !page_table || !seq_lens || !region_base)
+        return MTV_ERR_NULL;
+    if (batch < 1 || batch > MTV_MAX_BATCH || max_kv < 1 || max_kv > MTV_MAX_KV || num_slots < 1 ||
+        num_slots > INT32_MAX)
+        return MTV_ERR_SHAPE;
+    if (!aligned(kv_pool, 16) || !aligned(page_table, 4) || !aligned(seq_lens, 4) ||
+        !aligned(region_base, 4))
+        return MTV_ERR_ALIGN;
+    const int cus = current_cu_count();
+    if (cus <= 0)
+        return MTV_ERR_HIP;
+    mtv::KvArgs a{batch, 0, max_kv, num_slots, kv_pool, page_table, seq_lens, nullptr, nullptr,
+                  region_base};
+    if (mtv::launch_kv_move(a, cus, stream) != hipSuccess)
+        return MTV_ERR_HIP;
+    return MTV_OK;
+}
+
 const char* mtv_status_string(int status)
 {
     switch (status) {

@@ -39,9 +39,23 @@ struct Args {
     int64_t num_slots;
 };
 
+// Arguments of the KV-row moves (accepted-path commit, whole-sequence move).
+struct KvArgs {
+    int batch, nodes, max_kv;
+    int64_t num_slots;
+    void* kv;
+    int32_t* page_table;
+    const int32_t* seq_lens;
+    const int32_t* accept_len;  // commit only
+    const int32_t* path;        // commit only
+    const int32_t* base;
+};
+
 hipError_t launch_split(const Plan& plan, const Args& a, hipStream_t stream);
 hipError_t launch_combine(const Plan& plan, const Args& a, hipStream_t stream);
 hipError_t launch_tree_mask(int batch, int nodes, const int32_t* parents, uint32_t* mask,
                             hipStream_t stream);
+hipError_t launch_kv_commit(const KvArgs& a, hipStream_t stream);
+hipError_t launch_kv_move(const KvArgs& a, int cus, hipStream_t stream);
 
 }  // namespace mtv

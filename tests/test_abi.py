@@ -128,3 +128,22 @@ def test_tree_mask_build_rejects_bad_arguments():
         assert lib.mla_tree_mask_build(b, n, V(good), V(good), None) == -2
     assert lib.mla_tree_mask_build(1, 8, V(good + 2), V(good), None) == -3
     assert lib.mla_tree_mask_build(1, 8, V(good), V(good + 1), None) == -3
+
+
+def test_kv_moves_reject_bad_arguments():
+    lib = M.load()
+    V = ctypes.c_void_p
+    g = V(1 << 20)
+    # commit: NULLs, shapes, alignment
+    assert lib.mla_kv_commit(1, 8, 100, 1000, None, g, g, g, g, g, None) == -1
+    assert lib.mla_kv_commit(1, 8, 100, 1000, g, g, g, g, None, g, None) == -1
+    for b, n, mkv, p in [(0, 8, 100, 1000), (1, 0, 100, 1000), (1, 65, 100, 1000), (1, 8, 7, 1000),
+                         (1, 8, 100, 0), (1, 8, 100, 1 << 31)]:
+        assert lib.mla_kv_commit(b, n, mkv, p, g, g, g, g, g, g, None) == -2
+    assert lib.mla_kv_commit(1, 8, 100, 1000, V((1 << 20) + 8), g, g, g, g, g, None) == -3
+    assert lib.mla_kv_commit(1, 8, 100, 1000, g, V((1 << 20) + 2), g, g, g, g, None) == -3
+    # defrag
+    assert lib.mla_kv_defrag(1, 100, 1000, g, None, g, g, None) == -1
+    for b, mkv, p in [(0, 100, 1000), (1, 0, 1000), (1, 100, 0)]:
+        assert lib.mla_kv_defrag(b, mkv, p, g, g, g, g, None) == -2
+    assert lib.mla_kv_defrag(1, 100, 1000, V((1 << 20) + 4), g, g, g, None) == -3
