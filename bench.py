@@ -15,7 +15,8 @@ Also reported on the same line:
                duration (HIP events around each launch), against 8 TB/s;
   call_us      p10 / p50 / p90 of per-call durations (HIP events);
   context_sweep the 61-layer stacked chain8 sweep (own pool per layer, one page
-               table per context): microseconds per layer and GB/s;
+               table per context): microseconds per layer and GB/s, with eager
+               launches and as one HIP-graph-captured step;
   other_configs 64 nodes x 64 heads at context 131072 (MFMA-bound: TFLOP/s
                against 2.5 PFLOP/s dense bf16) and batch 8 with log-uniform
                contexts in both page layouts (GB/s each; outputs bitwise equal);
@@ -370,12 +371,36 @@ def sweep(args, torch, M, I):
         us_layer = step_s / LAYERS * 1e6
         b_layer = I.algorithmic_bytes([S], 8, 8)
         gbps = b_layer / (us_layer * 1e-6) / 1e9
+        # the same 61-layer step captured once into a HIP graph and replayed
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for c in calls:
+                c.run()
+        torch.cuda.current_stream().wait_stream(side)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for c in calls:
+                c.run()
+        graph.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            graph.replay()
+        torch.cuda.synchronize()
+        gstep_s = (time.perf_counter() - t0) / steps
         results.append({"context": ctx, "layers": LAYERS, "us_per_layer": round(us_layer, 3),
                         "ms_per_step": round(step_s * 1e3, 4), "gbps": round(gbps, 1),
                         "pct_of_peak": round(100 * gbps / PEAK_GBPS, 2),
                         "bytes_per_step": LAYERS * b_layer,
-                        "tokens_per_s_equiv": round(1.0 / step_s, 2)})
-        log("sweep ctx %d: %.2f us/layer, %.0f GB/s" % (ctx, us_layer, gbps))
+                        "tokens_per_s_equiv": round(1.0 / step_s, 2),
+                        "captured": {"us_per_layer": round(gstep_s / LAYERS * 1e6, 3),
+                                     "ms_per_step": round(gstep_s * 1e3, 4),
+                                     "gbps": round(b_layer * LAYERS / gstep_s / 1e9, 1),
+                                     "tokens_per_s_equiv": round(1.0 / gstep_s, 2)}})
+        log("sweep ctx %d: %.2f us/layer, %.0f GB/s (graph-captured step: %.2f us/layer)"
+            % (ctx, us_layer, gbps, gstep_s / LAYERS * 1e6))
+        del graph
         del calls
     return results
 

@@ -214,3 +214,54 @@ def test_graph_capture_replays_match_eager():
         torch.cuda.synchronize()
         assert torch.equal(out.view(torch.int16), eager[0].view(torch.int16))
         assert torch.equal(lse, eager[1])
+
+
+def test_captured_multi_layer_step_with_mask_build():
+    """A verify step captured as one graph: the mask build from the parent
+    array, then 6 layers (own pool and queries, one shared page table and
+    workspace). Every replay, with eager work in between, equals eager."""
+    base = I.make_workload(batch=1, num_nodes=16, num_heads=8, prefix_lens=[7000],
+                           num_slots=16384, tree="random", max_depth=5, config_id=109, device="cuda")
+    parents = torch.from_numpy(np.ascontiguousarray(base.parents, dtype=np.int32)).cuda()
+    mask = torch.zeros_like(base.tree_mask)
+    layers = [I.make_workload(batch=1, num_nodes=16, num_heads=8, prefix_lens=[7000],
+                              num_slots=16384, tree="random", max_depth=5, config_id=109,
+                              layer=l, device="cuda") for l in range(6)]
+    ws = None
+    calls = []
+    for wl in layers:
+        c = M.PreparedCall(wl.q, wl.kv_pool, base.page_table, base.seq_lens, mask, wl.scale,
+                           workspace=ws)
+        ws = c.workspace
+        calls.append(c)
+
+    def step():
+        M.tree_mask_build(parents, out=mask)
+        for c in calls:
+            c.run()
+
+    step()
+    torch.cuda.synchronize()
+    assert torch.equal(mask, base.tree_mask)  # the device-built mask is the generator's
+    eager = [(c.out.clone(), c.lse.clone()) for c in calls]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    other = I.config_workload(1, device="cuda")
+    for _ in range(3):
+        mask.zero_()
+        for c in calls:
+            c.out.zero_()
+            c.lse.zero_()
+        g.replay()
+        M.verify_workload(other)  # eager work between replays
+        torch.cuda.synchronize()
+        for c, (o, l) in zip(calls, eager):
+            assert torch.equal(c.out.view(torch.int16), o.view(torch.int16))
+            assert torch.equal(c.lse.view(torch.int32), l.view(torch.int32))
