@@ -165,8 +165,9 @@ def headline(args, torch, M, I):
 
 def other_configs(args, torch, M, I):
     """The all-heads configuration (64 nodes x 64 heads, MFMA-bound), the
-    batch-8 mixed-length configuration in both page layouts, and the tree-mask
-    build from parent arrays."""
+    batch-8 mixed-length configuration in three page layouts (scattered,
+    runs of 64, hybrid pages of 64), and the tree-mask build from parent
+    arrays."""
     out = {}
     names = [c.strip() for c in args.configs.split(",") if c.strip()]
     if "c4" in names:
@@ -227,10 +228,43 @@ def other_configs(args, torch, M, I):
             log("batch8-loguniform %s: %.2f us/call, %.0f GB/s" % (layout, med, b / (med * 1e-6) / 1e9))
             del c, wl
             torch.cuda.empty_cache()
-        del base
-        a, bb = outs["scattered"], outs["runs64"]
-        res["bitwise_equal"] = bool(torch.equal(a[0].view(torch.int16), bb[0].view(torch.int16))
-                                    and torch.equal(a[1].view(torch.int32), bb[1].view(torch.int32)))
+        # hybrid paging: prefixes in whole pages of 64 slots, tree rows at
+        # scattered slots, addressed by page list + tree slot list
+        log("building batch8-loguniform (hybrid pages of 64)")
+        hl = I.hybrid_layout(base, 64, seed=64)
+        w = hl.workload
+        out_t = torch.empty((w.batch, w.num_nodes, w.num_heads, 512), dtype=torch.bfloat16, device="cuda")
+        lse_t = torch.empty((w.batch, w.num_nodes, w.num_heads), dtype=torch.float32, device="cuda")
+        ws_t = torch.empty(M.workspace_size(M.make_shape(w.batch, w.num_nodes, w.num_heads, w.max_kv,
+                                                         w.num_slots)), dtype=torch.uint8, device="cuda")
+
+        class _Paged:
+            def run(self):
+                M.mla_tree_verify_paged(w.q, w.kv_pool, hl.prefix_pages, hl.tree_slots, w.seq_lens,
+                                        w.tree_mask, w.scale, 64, w.max_kv, out=out_t, lse=lse_t,
+                                        workspace=ws_t)
+        _Paged().run()
+        torch.cuda.synchronize()
+        outs["paged64"] = (out_t.clone(), lse_t.clone())
+        us = time_each_call([_Paged()], args.steps, torch)
+        seq = w.seq_lens_host()
+        b = I.algorithmic_bytes(seq, w.num_nodes, w.num_heads)
+        med = pct(us, 0.5)
+        res["paged64"] = {"us_per_call": {"p10": round(pct(us, 0.1), 2), "p50": round(med, 2),
+                                          "p90": round(pct(us, 0.9), 2)},
+                          "gbps": round(b / (med * 1e-6) / 1e9, 1),
+                          "pct_of_peak": round(100 * b / (med * 1e-6) / 1e9 / PEAK_GBPS, 2),
+                          "bytes_per_call": b, "page_size": 64,
+                          "page_list_entries": int(hl.prefix_pages.numel())}
+        log("batch8-loguniform paged64: %.2f us/call, %.0f GB/s" % (med, b / (med * 1e-6) / 1e9))
+        del hl, w, out_t, lse_t, ws_t, base
+        torch.cuda.empty_cache()
+
+        def same(x, y):
+            return bool(torch.equal(x[0].view(torch.int16), y[0].view(torch.int16))
+                        and torch.equal(x[1].view(torch.int32), y[1].view(torch.int32)))
+        res["bitwise_equal"] = same(outs["scattered"], outs["runs64"]) and same(outs["scattered"],
+                                                                              outs["paged64"])
         out["batch8-loguniform"] = res
     if "mask" in names:
         # the tree-mask build before the verify step (parent array -> bitmask)

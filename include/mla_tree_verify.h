@@ -129,6 +129,46 @@ int mla_tree_verify(const mtv_shape* shape,
                     hipStream_t stream);
 
 /*
+ * mla_tree_verify with hybrid paging of the key positions: the prefix goes
+ * through pages of page_size slots, the tree block through a per-token list.
+ * The pages propose larger pages for the prefix while the draft tree stays
+ * fine-grained ("The 130x Slowdown: Diagnosing Latency-Bound Decode in
+ * Speculative Decoding on Blackwell GPUs", The Broader Implications: What
+ * This Diagnosis Means), i.e. the contiguous prefix read in page-sized runs and only the
+ * tree block addressed per token ("The Moment of Certainty", The Path Forward:
+ * From Diagnosis to Solution).
+ *
+ * Key position p of sequence b (S_b = seq_lens[b], t0 = S_b - N) lives at
+ *   p <  t0:  prefix_pages[b][p / page_size] * page_size + p % page_size
+ *   p >= t0:  tree_slots[b][p - t0]           (tree node p - t0)
+ * and everything else is exactly mla_tree_verify: the result equals an
+ * mla_tree_verify call whose page_table holds those slots, bit for bit.
+ *   page_size    in [1, MTV_MAX_KV] (64 is the pages' figure)
+ *   max_pages    row length of prefix_pages, >= ceil((max_kv - N) / page_size)
+ *                for every position to have a page; a page number beyond the
+ *                row reads its last entry
+ *   prefix_pages int32 [B][max_pages], tree_slots int32 [B][N] (device,
+ *                4-byte aligned)
+ * Slots are clamped to [0, num_slots) like page indices. Workspace, other
+ * arguments and errors are those of mla_tree_verify (page_table is not used).
+ */
+int mla_tree_verify_paged(const mtv_shape* shape,
+                          int32_t page_size,
+                          int32_t max_pages,
+                          const void* q,
+                          const void* kv_pool,
+                          const int32_t* prefix_pages,
+                          const int32_t* tree_slots,
+                          const int32_t* seq_lens,
+                          const uint32_t* tree_mask,
+                          float scale,
+                          void* out,
+                          float* lse,
+                          void* workspace,
+                          size_t workspace_bytes,
+                          hipStream_t stream);
+
+/*
  * The two phases of mla_tree_verify, for callers that time them apart or that
  * merge slice partials themselves (for instance slices computed on several
  * devices, each holding part of a sequence's key positions).

@@ -20,7 +20,7 @@ STATUS_NAMES = {0: "MTV_OK", -1: "MTV_ERR_NULL", -2: "MTV_ERR_SHAPE", -3: "MTV_E
                 -4: "MTV_ERR_WORKSPACE", -5: "MTV_ERR_HIP"}
 EXPORTED = ("mla_tree_verify", "mla_tree_verify_workspace_size", "mtv_status_string",
             "mtv_plan_query", "mla_tree_verify_splitkv", "mla_tree_verify_combine",
-            "mla_tree_mask_build", "mla_kv_commit", "mla_kv_defrag")
+            "mla_tree_mask_build", "mla_kv_commit", "mla_kv_defrag", "mla_tree_verify_paged")
 
 
 class MtvShape(ctypes.Structure):
@@ -69,6 +69,9 @@ def load(path: Optional[str] = None):
     lib.mla_tree_mask_build.restype = ctypes.c_int
     lib.mla_tree_mask_build.argtypes = [ctypes.c_int32, ctypes.c_int32, VP, VP, VP]
     I32, I64 = ctypes.c_int32, ctypes.c_int64
+    lib.mla_tree_verify_paged.restype = ctypes.c_int
+    lib.mla_tree_verify_paged.argtypes = [SP, I32, I32, VP, VP, VP, VP, VP, VP, ctypes.c_float, VP,
+                                          VP, VP, ctypes.c_size_t, VP]
     lib.mla_kv_commit.restype = ctypes.c_int
     lib.mla_kv_commit.argtypes = [I32, I32, I32, I64, VP, VP, VP, VP, VP, VP, VP]
     lib.mla_kv_defrag.restype = ctypes.c_int
@@ -210,6 +213,60 @@ def tree_mask_build(parents: torch.Tensor, out: Optional[torch.Tensor] = None, s
     if rc != MTV_OK:
         raise MtvError(rc, status_string(rc))
     return out
+
+
+def mla_tree_verify_paged(q: torch.Tensor, kv_pool: torch.Tensor, prefix_pages: torch.Tensor,
+                          tree_slots: torch.Tensor, seq_lens: torch.Tensor, tree_mask: torch.Tensor,
+                          scale: float, page_size: int, max_kv: int,
+                          out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                          workspace: Optional[torch.Tensor] = None, stream=None):
+    """Tree-verify attention with hybrid paging (see mla_tree_verify_paged):
+    prefix_pages int32 [B, max_pages] (pages of page_size slots), tree_slots
+    int32 [B, N]; max_kv bounds every sequence length. Returns (out, lse)."""
+    if q.dim() != 4:
+        raise ValueError("q must be [B, N, H, 576]")
+    B, N, H, D = q.shape
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("q must be on a GPU")
+    if kv_pool.dim() != 2 or prefix_pages.dim() != 2:
+        raise ValueError("kv_pool must be [num_slots, 576] and prefix_pages [B, max_pages]")
+    P = kv_pool.shape[0]
+    max_pages = prefix_pages.shape[1]
+    W = (N + 31) // 32
+    _check(q, "q", torch.bfloat16, (B, N, H, 576), dev)
+    _check(kv_pool, "kv_pool", torch.bfloat16, (P, 576), dev)
+    _check(prefix_pages, "prefix_pages", torch.int32, (B, max_pages), dev)
+    _check(tree_slots, "tree_slots", torch.int32, (B, N), dev)
+    _check(seq_lens, "seq_lens", torch.int32, (B,), dev)
+    if tree_mask.dtype not in (torch.int32, getattr(torch, "uint32", torch.int32)):
+        raise TypeError("tree_mask must hold 32-bit words")
+    _check(tree_mask, "tree_mask", tree_mask.dtype, (B, N, W), dev)
+    if out is None:
+        out = torch.empty((B, N, H, 512), dtype=torch.bfloat16, device=dev)
+    else:
+        _check(out, "out", torch.bfloat16, (B, N, H, 512), dev)
+    if lse is None:
+        lse = torch.empty((B, N, H), dtype=torch.float32, device=dev)
+    else:
+        _check(lse, "lse", torch.float32, (B, N, H), dev)
+    shape = make_shape(B, N, H, max_kv, P)
+    lib = load()
+    with torch.cuda.device(dev):
+        need = int(lib.mla_tree_verify_workspace_size(ctypes.byref(shape)))
+        if need == 0:
+            raise MtvError(-2, status_string(-2))
+        if workspace is None or workspace.numel() * workspace.element_size() < need:
+            workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+        rc = lib.mla_tree_verify_paged(ctypes.byref(shape), int(page_size), int(max_pages), _ptr(q),
+                                       _ptr(kv_pool), _ptr(prefix_pages), _ptr(tree_slots),
+                                       _ptr(seq_lens), _ptr(tree_mask), ctypes.c_float(scale),
+                                       _ptr(out), _ptr(lse), _ptr(workspace),
+                                       ctypes.c_size_t(workspace.numel() * workspace.element_size()),
+                                       _stream_handle(dev, stream))
+    if rc != MTV_OK:
+        raise MtvError(rc, status_string(rc))
+    return out, lse
 
 
 def _stream_handle(dev, stream):

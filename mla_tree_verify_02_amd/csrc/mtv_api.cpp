@@ -107,17 +107,34 @@ enum Phase { kSplit = 1, kCombine = 2 };
 
 // Shared validation and dispatch of the three launching entry points. Pointers
 // a phase does not use may be NULL for that phase.
+// Hybrid paging of the split phase (prefix_pages == NULL: per-token table).
+struct Paging {
+    const int32_t* prefix_pages = nullptr;
+    const int32_t* tree_slots = nullptr;
+    int page_size = 0, max_pages = 0;
+};
+
 int run(int phases, const mtv_shape* shape, const void* q, const void* kv_pool,
         const int32_t* page_table, const int32_t* seq_lens, const uint32_t* tree_mask,
         float scale, void* out, float* lse, void* workspace, size_t workspace_bytes,
-        hipStream_t stream)
+        hipStream_t stream, const Paging& pg = Paging())
 {
     const bool split = phases & kSplit;
     const bool combine = phases & kCombine;
+    const bool paged = pg.prefix_pages || pg.tree_slots;
     if (!shape || !seq_lens || !workspace)
         return MTV_ERR_NULL;
-    if (split && (!q || !kv_pool || !page_table || !tree_mask))
+    if (split && (!q || !kv_pool || !tree_mask))
         return MTV_ERR_NULL;
+    if (split && !paged && !page_table)
+        return MTV_ERR_NULL;
+    if (split && paged && (!pg.prefix_pages || !pg.tree_slots))
+        return MTV_ERR_NULL;
+    if (paged && (pg.page_size < 1 || pg.page_size > MTV_MAX_KV || pg.max_pages < 1 ||
+                  pg.max_pages > MTV_MAX_KV))
+        return MTV_ERR_SHAPE;
+    if (paged && (!aligned(pg.prefix_pages, 4) || !aligned(pg.tree_slots, 4)))
+        return MTV_ERR_ALIGN;
     if (combine && (!out || !lse))
         return MTV_ERR_NULL;
     if (!shape_ok(*shape) || (split && !std::isfinite(scale)))
@@ -125,7 +142,7 @@ int run(int phases, const mtv_shape* shape, const void* q, const void* kv_pool,
     if (!aligned(seq_lens, 4) || !aligned(workspace, 256))
         return MTV_ERR_ALIGN;
     if (split && (!aligned(q, 16) || !aligned(kv_pool, 16) || !aligned(page_table, 4) ||
-                  !aligned(tree_mask, 4)))
+                  !aligned(tree_mask, 4)))  // page_table may be NULL when paged
         return MTV_ERR_ALIGN;
     if (combine && (!aligned(out, 16) || !aligned(lse, 4)))
         return MTV_ERR_ALIGN;
@@ -152,6 +169,10 @@ int run(int phases, const mtv_shape* shape, const void* q, const void* kv_pool,
     a.heads = shape->num_heads;
     a.max_kv = shape->max_kv;
     a.num_slots = shape->num_slots;
+    a.prefix_pages = pg.prefix_pages;
+    a.tree_slots = pg.tree_slots;
+    a.page_size = pg.page_size;
+    a.max_pages = pg.max_pages;
     if (split && mtv::launch_split(plan, a, stream) != hipSuccess)
         return MTV_ERR_HIP;
     if (combine && mtv::launch_combine(plan, a, stream) != hipSuccess)
@@ -173,6 +194,23 @@ int mla_tree_verify(const mtv_shape* shape, const void* q, const void* kv_pool,
         return MTV_ERR_NULL;
     return run(kSplit | kCombine, shape, q, kv_pool, page_table, seq_lens, tree_mask, scale, out,
                lse, workspace, workspace_bytes, stream);
+}
+
+int mla_tree_verify_paged(const mtv_shape* shape, int32_t page_size, int32_t max_pages,
+                          const void* q, const void* kv_pool, const int32_t* prefix_pages,
+                          const int32_t* tree_slots, const int32_t* seq_lens,
+                          const uint32_t* tree_mask, float scale, void* out, float* lse,
+                          void* workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    if (!out || !lse || !q || !kv_pool || !prefix_pages || !tree_slots || !tree_mask)
+        return MTV_ERR_NULL;
+    Paging pg;
+    pg.prefix_pages = prefix_pages;
+    pg.tree_slots = tree_slots;
+    pg.page_size = page_size;
+    pg.max_pages = max_pages;
+    return run(kSplit | kCombine, shape, q, kv_pool, nullptr, seq_lens, tree_mask, scale, out, lse,
+               workspace, workspace_bytes, stream, pg);
 }
 
 int mla_tree_verify_splitkv(const mtv_shape* shape, const void* q, const void* kv_pool,

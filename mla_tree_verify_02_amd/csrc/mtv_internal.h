@@ -37,6 +37,10 @@ struct Args {
     float* part_ml;  // [B][G][splits][64 rows][2]  (running max in log2 units, sum)
     int batch, nodes, heads, max_kv;
     int64_t num_slots;
+    // hybrid paging (NULL prefix_pages: the per-token page_table is used)
+    const int32_t* prefix_pages;  // [B][max_pages] pages of page_size slots
+    const int32_t* tree_slots;    // [B][N] slot of each tree node
+    int page_size, max_pages;
 };
 
 // Arguments of the KV-row moves (accepted-path commit, whole-sequence move).

@@ -94,6 +94,13 @@ __host__ __device__ inline int xcd_block(int items, int row_groups)
     return per;
 }
 
+// kPaged selects how a key position finds its pool slot: false, through the
+// per-token page table (slot = page_table[b][p]); true, the hybrid layout, in
+// which prefix positions go through pages of page_size slots
+// (slot = prefix_pages[b][p / page_size] * page_size + p % page_size) and the
+// N tree positions through a per-token list (slot = tree_slots[b][p - (S - N)]).
+// The two differ only in the index staging below.
+template <bool kPaged>
 __global__ __launch_bounds__(kThreads, 1) void split_kernel(Args a, int splits, int chunk,
                                                             int row_groups, float scale_log2)
 {
@@ -131,21 +138,36 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(Args a, int splits, 
     const int nkeys = min(chunk, S - k0);
     const int ntiles = (nkeys + kTileKeys - 1) / kTileKeys;
 
-    // Stage the slice's page indices in windows of 128 tiles: window w (tiles
+    // Stage the slice's pool slots in windows of 128 tiles: window w (tiles
     // 128w .. 128w+127) into s_idx[w % 2]. Positions past the end reuse the
-    // last valid position's row (finite data, weight zero); indices are
-    // clamped so that no gather leaves the pool. Window 0 is staged here; a
-    // slice longer than one window stages window w+1 halfway through window w.
+    // last valid position's row (finite data, weight zero); slots (and page
+    // numbers) are clamped so that no read leaves its buffer. Window 0 is
+    // staged here; a slice longer than one window stages window w+1 halfway
+    // through window w.
     const int32_t* pt = a.page_table + (int64_t)b * a.max_kv;
     const int maxslot = (int)(a.num_slots - 1);
     const int nwin = (ntiles + kWinTiles - 1) / kWinTiles;
+    auto slot_of = [&](int p) -> int {
+        int64_t v;
+        if constexpr (kPaged) {
+            const int t0 = S - N;
+            if (p < t0) {
+                const int pg = min(p / a.page_size, a.max_pages - 1);
+                v = (int64_t)a.prefix_pages[(int64_t)b * a.max_pages + pg] * a.page_size +
+                    (p - (p / a.page_size) * a.page_size);
+            } else {
+                v = a.tree_slots[(int64_t)b * N + (p - t0)];
+            }
+        } else {
+            v = pt[p];
+        }
+        return (int)(v < 0 ? 0 : (v > maxslot ? maxslot : v));
+    };
     auto stage = [&](int w) {
         const int n = min(ntiles * kTileKeys - w * kWinKeys, kWinKeys);
         int* dst = s_idx[w & 1];
-        for (int i = tid; i < n; i += kThreads) {
-            const int v = pt[min(k0 + w * kWinKeys + i, S - 1)];
-            dst[i] = v < 0 ? 0 : (v > maxslot ? maxslot : v);
-        }
+        for (int i = tid; i < n; i += kThreads)
+            dst[i] = slot_of(min(k0 + w * kWinKeys + i, S - 1));
     };
     stage(0);
 
@@ -562,7 +584,7 @@ hipError_t launch_split(const Plan& p, const Args& a, hipStream_t stream)
 {
     const float scale_log2 = (float)((double)a.scale * 1.4426950408889634);
     const int per_xcd = xcd_block(p.splits * p.row_groups, p.row_groups);
-    hipLaunchKernelGGL(split_kernel, dim3(8 * per_xcd, a.batch), dim3(kThreads), 0,
+    hipLaunchKernelGGL(a.prefix_pages ? split_kernel<true> : split_kernel<false>, dim3(8 * per_xcd, a.batch), dim3(kThreads), 0,
                        stream, a, p.splits, p.chunk, p.row_groups, scale_log2);
     return hipGetLastError();
 }

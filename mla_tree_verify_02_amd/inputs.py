@@ -394,6 +394,67 @@ def relayout(wl: Workload, table_seed: int, layout: str) -> Workload:
     return other
 
 
+@dataclass
+class HybridLayout:
+    """A workload's rows under hybrid paging: prefix positions in pages of
+    page_size slots, tree nodes at scattered slots. `workload` holds the
+    relaid pool and the equivalent per-token table."""
+    workload: Workload
+    prefix_pages: torch.Tensor  # int32 [B, max_pages]
+    tree_slots: torch.Tensor    # int32 [B, N]
+    page_size: int
+
+
+def hybrid_layout(wl: Workload, page_size: int, seed: int) -> HybridLayout:
+    """The same logical inputs with the prefix of each sequence in whole pages
+    of `page_size` slots (page numbers from a seeded permutation of the pool's
+    pages) and its N tree rows at seeded scattered slots outside those pages.
+    Unreferenced slots hold NaN; unused page entries are 0."""
+    P = wl.num_slots
+    g = _gen(seed, "cpu")
+    npages = P // page_size
+    pperm = torch.randperm(npages, generator=g).numpy().astype(np.int64)
+    N = wl.num_nodes
+    seqs = wl.seq_lens_host()
+    max_pages = max(1, max((s - N + page_size - 1) // page_size for s in seqs))
+    pages = np.zeros((wl.batch, max_pages), dtype=np.int64)
+    used = np.zeros(P, dtype=bool)
+    pg = 0
+    for b, s in enumerate(seqs):
+        need = (s - N + page_size - 1) // page_size
+        if pg + need > npages:
+            raise ValueError("pool too small for the prefixes")
+        pages[b, :need] = pperm[pg:pg + need]
+        for q in pperm[pg:pg + need]:
+            used[q * page_size:(q + 1) * page_size] = True
+        pg += need
+    free = np.nonzero(~used)[0]
+    free = free[torch.randperm(len(free), generator=g).numpy()]
+    if len(free) < wl.batch * N:
+        raise ValueError("pool too small for the tree rows")
+    tree = free[:wl.batch * N].reshape(wl.batch, N)
+    table = np.zeros((wl.batch, wl.max_kv), dtype=np.int64)
+    for b, s in enumerate(seqs):
+        t0 = s - N
+        p = np.arange(t0)
+        table[b, :t0] = pages[b, p // page_size] * page_size + p % page_size
+        table[b, t0:s] = tree[b]
+        table[b, s:] = tree[b, 0]  # never read (positions >= S)
+    dev = wl.q.device
+    old = wl.kv_pool.view(torch.int16)
+    new = torch.full_like(old, BF16_NAN_BITS)
+    t_old = wl.page_table.long()
+    t_new = torch.from_numpy(table).to(dev)
+    for b, s in enumerate(seqs):
+        new[t_new[b, :s]] = old[t_old[b, :s]]
+    out = Workload(q=wl.q.clone(), kv_pool=new.view(torch.bfloat16),
+                   page_table=t_new.to(torch.int32), seq_lens=wl.seq_lens.clone(),
+                   tree_mask=wl.tree_mask.clone(), parents=wl.parents, scale=wl.scale,
+                   prefix_lens=list(wl.prefix_lens), name=f"{wl.name}-paged{page_size}")
+    return HybridLayout(out, torch.from_numpy(pages.astype(np.int32)).to(dev),
+                        torch.from_numpy(tree.astype(np.int32)).to(dev), page_size)
+
+
 def algorithmic_bytes(seq_lens: Sequence[int], num_nodes: int, num_heads: int) -> int:
     """Bytes a call must move at minimum: every referenced 1152-byte KV row once
     and its 4-byte page index, Q in, out and lse out, and the mask."""

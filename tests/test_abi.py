@@ -147,3 +147,24 @@ def test_kv_moves_reject_bad_arguments():
     for b, mkv, p in [(0, 100, 1000), (1, 0, 1000), (1, 100, 0)]:
         assert lib.mla_kv_defrag(b, mkv, p, g, g, g, g, None) == -2
     assert lib.mla_kv_defrag(1, 100, 1000, V((1 << 20) + 4), g, g, g, None) == -3
+
+
+def test_paged_entry_rejects_bad_arguments():
+    lib = M.load()
+    V = ctypes.c_void_p
+    g = 1 << 20
+    s = M.make_shape(1, 8, 8, 1032, 4096)
+
+    def call(ps=64, mp=17, pages=g, tree=g, q=g, scale=0.07):
+        return lib.mla_tree_verify_paged(ctypes.byref(s), ps, mp, V(q), V(g), V(pages), V(tree),
+                                         V(g), V(g), ctypes.c_float(scale), V(g), V(g), V(g),
+                                         ctypes.c_size_t(1 << 30), None)
+
+    assert call(pages=None) == -1
+    assert call(tree=None) == -1
+    assert call(q=None) == -1
+    for ps, mp in [(0, 17), (-64, 17), (64, 0), (64, -1), (1 << 30, 17)]:
+        assert call(ps=ps, mp=mp) == -2, (ps, mp)
+    assert call(scale=float("nan")) == -2
+    assert call(pages=g + 2) == -3
+    assert call(tree=g + 1) == -3
