@@ -269,8 +269,6 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(Args a, int splits, 
         load_idx(1, idx_n);
         issue(1, idx_n);
     }
-    if (ntiles > 2)
-        load_idx(2, idx_n);
 
     constexpr int kKGroup = 6;            // K-operand reads per group (double-buffered)
     constexpr int kKReads = 2 * kKSteps;  // 36 per tile (two key blocks)
@@ -289,12 +287,10 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(Args a, int splits, 
         else
             wait_vmcnt<0>();
         __syncthreads();
-        if (t + 2 < ntiles)
-            issue(t + 2, idx_n);
         if (t % kWinTiles == kWinTiles / 2 && t / kWinTiles + 1 < nwin)
             stage(t / kWinTiles + 1);
-        if (t + 3 < ntiles)
-            load_idx(t + 3, idx_n);
+        if (t + 2 < ntiles)
+            load_idx(t + 2, idx_n);
     };
 
     int t = 0;
@@ -307,6 +303,14 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(Args a, int splits, 
             const char LDS_AS* kb0 = buf + koff0;
             const char LDS_AS* kb1 = buf + koff1;
             const int base = k0 + t * kTileKeys;
+            // Tile t+2's rows go into the buffer tile t-1 used, spread over
+            // this tile's Q.K^T so that the address unit works while the MFMAs
+            // issue. Past the last tile (and when a raised reference makes
+            // this tile run again) the same loads go out again from the last
+            // staged indices into that free buffer: identical or never-read
+            // bytes, rows already in L2, and waits that only get stricter.
+            const uint32_t gdst = lds0 + (uint32_t)(((t + 2) % kStages) * kTileBytes +
+                                                    wave * (kKeysPerWave * kRowBytes));
 
             // S^T = K.Q^T for key blocks 0 and 1 (keys kb*16 + 4*lg + i against
             // row rl), two interleaved MFMA chains fed by double-buffered groups
@@ -328,6 +332,10 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(Args a, int splits, 
                         kf[(g + 1) & 1][j] =
                             *(const bf16x8 LDS_AS*)kptr((g + 1) * kKGroup + j);
                 }
+                // gathers of tile t+2, 1-2 per group (loads 3g/2 .. 3(g+1)/2 - 1)
+#pragma unroll
+                for (int j = 3 * g / 2; j < 3 * (g + 1) / 2; ++j)
+                    gather16_to_lds(kv + (int64_t)idx_n[j] * kRowBytes + gco[j], gdst + j * 1024);
 #pragma unroll
                 for (int j = 0; j < kKGroup; ++j) {
                     const int n = g * kKGroup + j;
@@ -446,6 +454,8 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(Args a, int splits, 
         for (int cb = 0; cb < kColBlocks; ++cb)
             o[cb] *= alpha;
     }
+
+    wait_vmcnt<0>();  // the last tiles' loads land before the workgroup ends
 
     // Partial result of this slice, in the register-fragment order.
     float l_tot = l_run + __shfl_xor(l_run, 16);
