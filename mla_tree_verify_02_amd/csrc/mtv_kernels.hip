@@ -332,10 +332,8 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(Args a, int splits, 
                         kf[(g + 1) & 1][j] =
                             *(const bf16x8 LDS_AS*)kptr((g + 1) * kKGroup + j);
                 }
-                // gathers of tile t+2, 1-2 per group (loads 3g/2 .. 3(g+1)/2 - 1)
-#pragma unroll
-                for (int j = 3 * g / 2; j < 3 * (g + 1) / 2; ++j)
-                    gather16_to_lds(kv + (int64_t)idx_n[j] * kRowBytes + gco[j], gdst + j * 1024);
+                // gathers of tile t+2: load g here, loads 6-8 in the P.V below
+                gather16_to_lds(kv + (int64_t)idx_n[g] * kRowBytes + gco[g], gdst + g * 1024);
 #pragma unroll
                 for (int j = 0; j < kKGroup; ++j) {
                     const int n = g * kKGroup + j;
@@ -419,6 +417,10 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(Args a, int splits, 
                         vt[(g + 1) & 1][2 * c + 1] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
                             (bf16x4 LDS_AS*)(vptr(cb) + 16 * kRowBytes));
                     }
+                }
+                if ((g & 1) && g < 7) {
+                    const int j = 6 + (g >> 1);
+                    gather16_to_lds(kv + (int64_t)idx_n[j] * kRowBytes + gco[j], gdst + j * 1024);
                 }
 #pragma unroll
                 for (int c = 0; c < kVGroup; ++c) {
