@@ -510,7 +510,8 @@ def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=200,
+                    help="untimed calls first (about 8 ms of work, so that clocks settle)")
     ap.add_argument("--rotate", type=int, default=8, help="independent input sets cycled over")
     ap.add_argument("--sweep", default="65536,189440",
                     help="contexts of the 61-layer chain8 sweep ('' to skip)")
