@@ -26,6 +26,10 @@
  * indices and the gathered 1152-byte rows in LDS, and runs Q.K^T and P.V on
  * bf16 MFMA with an online softmax in fp32), then a log-sum-exp combine kernel
  * that merges the slices and writes out and lse. Both are enqueued on `stream`.
+ * Slices are balanced over the whole batch from seq_lens on the device: every
+ * sequence is cut into slices of the same number of 32-key tiles, sized from
+ * the batch's total, so a long sequence gets many slices and a short one few
+ * (a batch of one sequence is sliced for max_kv keys).
  */
 #ifndef MLA_TREE_VERIFY_H
 #define MLA_TREE_VERIFY_H
@@ -175,13 +179,13 @@ int mla_tree_verify_paged(const mtv_shape* shape,
  *
  * mla_tree_verify_splitkv enqueues only the split-KV kernel: it takes the same
  * inputs as mla_tree_verify and leaves, in `workspace`, one partial per
- * (sequence, 64-row group, key slice): the unnormalised weighted latent sum
+ * (64-row group, key slice of the batch): the unnormalised weighted latent sum
  * (stored as bf16, 1024 B per row), the running max of the scaled scores in
  * log2 units and the sum of 2^(score*log2(e) - max) (fp32, 8 B per row).
  * mla_tree_verify_combine merges those partials by
  * log-sum-exp and writes out and lse. The combine must run on a workspace
- * filled by a splitkv call with the same shape on the same device (the layout
- * follows mtv_plan_query), ordered after it on a stream. Arguments, alignment
+ * filled by a splitkv call with the same shape, seq_lens and device, ordered
+ * after it on a stream (both derive the slicing from seq_lens). Arguments, alignment
  * and error codes are those of mla_tree_verify; mla_tree_verify is exactly
  * the splitkv call followed by the combine call on the same stream.
  */
@@ -296,9 +300,12 @@ const char* mtv_status_string(int status);
 
 /*
  * Introspection of the split plan the library uses for `shape` on a device with
- * `num_cus` compute units: key slices per sequence (*splits), keys per slice
- * (*chunk, a multiple of 32) and 64-row groups per sequence (*row_groups).
- * Host-only arithmetic. Returns MTV_OK, MTV_ERR_NULL or MTV_ERR_SHAPE.
+ * `num_cus` compute units, for a batch whose sequences all hold max_kv keys:
+ * key slices per sequence (*splits), keys per slice (*chunk, a multiple of 32)
+ * and 64-row groups per sequence (*row_groups). Batches of other lengths are
+ * sliced on the device from seq_lens with the same rule (slices of one size
+ * for the whole batch, sized from its total key count). Host-only arithmetic.
+ * Returns MTV_OK, MTV_ERR_NULL or MTV_ERR_SHAPE.
  */
 int mtv_plan_query(const mtv_shape* shape, int num_cus, int* splits, int* chunk, int* row_groups);
 

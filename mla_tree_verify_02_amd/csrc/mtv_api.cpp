@@ -47,23 +47,40 @@ size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 // The plan: enough slices per sequence that the batch's (sequence, row group)
 // pairs give about one workgroup per compute unit, each slice a whole number of
 // 32-key tiles.
+// The batch's key positions are cut into slices of c whole tiles, one c for
+// every sequence, sized from the total: G slice slots per row group (about
+// one workgroup per compute unit), c = ceil(T / G') for T tiles in the batch
+// with G' = G - (B - 1) when that is at least G / 2 (else G), so the slices of
+// all sequences number at most G (at most G + B in the other case) and none
+// is longer than the others. The kernels derive c and each slice's sequence
+// from seq_lens on the device; the host only bounds the slice count for the
+// grid and the workspace.
 mtv::Plan make_plan(const mtv_shape& s, int cus)
 {
     mtv::Plan p{};
     p.rows = s.num_nodes * s.num_heads;
     p.row_groups = (p.rows + mtv::kRowsPerGroup - 1) / mtv::kRowsPerGroup;
+    int64_t slots = ((int64_t)cus + p.row_groups - 1) / p.row_groups;
+    if (slots < 1)
+        slots = 1;
+    p.slots = (int)slots;
+    // slices of the whole batch: at most G when the target is reduced (always
+    // for one sequence), at most G + B otherwise; the grid and the workspace
+    // are sized by this bound, so a tight one keeps every workgroup resident
+    const bool reduced = slots > 2 * ((int64_t)s.batch - 1);
+    // the slicing of a batch whose sequences all hold max_kv keys
     const int64_t tiles = (s.max_kv + mtv::kTileKeys - 1) / mtv::kTileKeys;
-    const int64_t pairs = (int64_t)s.batch * p.row_groups;
-    int64_t splits = (cus + pairs - 1) / pairs;
-    if (splits < 1)
-        splits = 1;
-    if (splits > tiles)
-        splits = tiles;
-    const int64_t chunk_tiles = (tiles + splits - 1) / splits;
-    splits = (tiles + chunk_tiles - 1) / chunk_tiles;
-    p.splits = (int)splits;
-    p.chunk = (int)(chunk_tiles * mtv::kTileKeys);
-    const size_t parts = (size_t)pairs * (size_t)p.splits;
+    const int64_t target = reduced ? slots - (s.batch - 1) : slots;
+    int64_t c = ((int64_t)s.batch * tiles + target - 1) / target;
+    if (c > tiles)
+        c = tiles;
+    p.splits = (int)((tiles + c - 1) / c);
+    p.chunk = (int)(c * mtv::kTileKeys);
+    // One sequence keeps that slicing whatever its length (a shorter one uses
+    // fewer of the slices), so the grid holds exactly the slices it can use.
+    p.single_c = (int)c;
+    p.max_slices = s.batch == 1 ? p.splits : (int)(reduced ? slots : slots + s.batch);
+    const size_t parts = (size_t)p.row_groups * (size_t)p.max_slices;
     p.part_o_off = 0;
     p.part_ml_off = align_up(parts * mtv::kRowsPerGroup * mtv::kDv * sizeof(uint16_t), 256);
     p.bytes = align_up(p.part_ml_off + parts * mtv::kRowsPerGroup * 2 * sizeof(float), 256);

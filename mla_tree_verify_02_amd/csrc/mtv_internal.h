@@ -19,8 +19,11 @@ constexpr int kRowsPerGroup = 64;  // query rows per split workgroup (4 waves x 
 struct Plan {
     int rows;          // R = N * H query rows per sequence
     int row_groups;    // ceil(R / 64)
-    int splits;        // key slices per sequence
-    int chunk;         // keys per slice, a multiple of kTileKeys
+    int slots;         // G: target key slices per row group over the whole batch
+    int max_slices;    // G + B: bound on the slices of all sequences together
+    int single_c;      // tiles per slice of a batch of one sequence (from max_kv)
+    int splits;        // slices per sequence when every sequence holds max_kv keys
+    int chunk;         // keys per slice in that case, a multiple of kTileKeys
     size_t part_o_off, part_ml_off, bytes;  // workspace layout
 };
 

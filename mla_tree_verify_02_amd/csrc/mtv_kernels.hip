@@ -94,6 +94,123 @@ __host__ __device__ inline int xcd_block(int items, int row_groups)
     return per;
 }
 
+// Length-balanced slicing, derived on the device from seq_lens by every
+// workgroup of both kernels (so they agree without any host round trip):
+// every sequence's key positions are cut into slices of c whole tiles, in
+// sequence order; slice k of sequence b is global slice start_b + k. With T
+// tiles in the batch and G slice slots per row group, c = ceil(T / G') where
+// G' = G - (B - 1) when that leaves more than half of G, else G' = G.
+// Rounding each sequence up to whole slices adds fewer than B slices, so the
+// total stays within G in the first case (one workgroup per slot; for one
+// sequence ceil(T / ceil(T / G)) <= G) and within G + B in the second.
+
+// Keys of sequence b: S_b clamped to [N, max_kv].
+__device__ __forceinline__ int seq_keys(const Args& a, int b)
+{
+    return min(max(a.seq_lens[b], a.nodes), a.max_kv);
+}
+
+// Tiles of sequence b: its keys in 32-key tiles.
+__device__ __forceinline__ int64_t seq_tiles(const Args& a, int b)
+{
+    return (seq_keys(a, b) + kTileKeys - 1) / kTileKeys;
+}
+
+// Sum of v over the workgroup's NT threads; every thread gets it. red holds
+// NT/64 words of LDS; the first barrier lets a previous call's readers finish.
+template <int NT>
+__device__ __forceinline__ int64_t block_sum(int64_t v, int64_t* red)
+{
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1)
+        v += __shfl_xor(v, o);
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0)
+        red[threadIdx.x >> 6] = v;
+    __syncthreads();
+    int64_t t = 0;
+#pragma unroll
+    for (int i = 0; i < NT / 64; ++i)
+        t += red[i];
+    return t;
+}
+
+// Exclusive prefix sum of v over the workgroup's threads in thread order;
+// total receives the sum over all of them.
+template <int NT>
+__device__ __forceinline__ int64_t block_excl_scan(int64_t v, int64_t* red, int64_t& total)
+{
+    const int lane = threadIdx.x & 63;
+    const int w = threadIdx.x >> 6;
+    int64_t x = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int64_t y = __shfl_up(x, o);
+        if (lane >= o)
+            x += y;
+    }
+    __syncthreads();
+    if (lane == 63)
+        red[w] = x;
+    __syncthreads();
+    int64_t before = 0, tot = 0;
+#pragma unroll
+    for (int i = 0; i < NT / 64; ++i) {
+        if (i < w)
+            before += red[i];
+        tot += red[i];
+    }
+    total = tot;
+    return before + x - v;
+}
+
+// Tiles per slice c and the number of slices of all sequences together.
+// sk and tb receive the keys and tiles of one sequence: of the batch's only
+// sequence when B = 1 (every thread), else of sequence threadIdx.x when
+// B <= NT (0 past the batch), else 0. A single sequence takes c from the host
+// (sized for max_kv, so that the grid holds exactly its slices) and needs no
+// reduction and no barrier; up to NT sequences need one load per thread.
+template <int NT>
+__device__ __forceinline__ void slicing(const Args& a, int slots, int single_c, int64_t* red,
+                                        int64_t& c, int64_t& nslices, int& sk, int64_t& tb)
+{
+    const int B = a.batch;
+    const int target = (slots > 2 * (B - 1)) ? slots - (B - 1) : slots;
+    if (__builtin_expect(B == 1, 1)) {  // laid out as the straight-line path
+        sk = seq_keys(a, 0);
+        const int t1 = (sk + kTileKeys - 1) / kTileKeys;  // < 2^21: 32-bit arithmetic
+        tb = t1;
+        c = single_c;
+        nslices = (t1 + single_c - 1) / single_c;
+        return;
+    }
+    int64_t t = 0;
+    sk = 0;
+    tb = 0;
+    if (B <= NT) {
+        if ((int)threadIdx.x < B) {
+            sk = seq_keys(a, threadIdx.x);
+            tb = (sk + kTileKeys - 1) / kTileKeys;
+        }
+        t = tb;
+    } else {
+        for (int b = threadIdx.x; b < B; b += NT)
+            t += seq_tiles(a, b);
+    }
+    const int64_t T = block_sum<NT>(t, red);
+    c = (T + target - 1) / target;
+    if (c < 1)
+        c = 1;
+    int64_t n = 0;
+    if (B <= NT) {
+        n = (tb + c - 1) / c;
+    } else {
+        for (int b = threadIdx.x; b < B; b += NT)
+            n += (seq_tiles(a, b) + c - 1) / c;
+    }
+    nslices = block_sum<NT>(n, red);
+}
+
 // kPaged selects how a key position finds its pool slot: false, through the
 // per-token page table (slot = page_table[b][p]); true, the hybrid layout, in
 // which prefix positions go through pages of page_size slots
@@ -101,28 +218,77 @@ __host__ __device__ inline int xcd_block(int items, int row_groups)
 // N tree positions through a per-token list (slot = tree_slots[b][p - (S - N)]).
 // The two differ only in the index staging below.
 template <bool kPaged>
-__global__ __launch_bounds__(kThreads, 1) void split_kernel(Args a, int splits, int chunk,
-                                                            int row_groups, float scale_log2)
+__global__ __launch_bounds__(kThreads, 1) void split_kernel(Args a, int slots, int single_c,
+                                                            int max_slices, int row_groups,
+                                                            float scale_log2)
 {
     __shared__ __attribute__((aligned(16))) char s_kv[kStages * kTileBytes];
     __shared__ int s_idx[2][kWinKeys];  // page indices, two windows of 128 tiles
+
+    __shared__ int64_t s_red[kWaves];
+    __shared__ int s_hit[3];
+
+    // This batch's slicing (see slicing()): c tiles per slice, nslices in all.
+    int64_t c, nslices, tb;
+    int sk;
+    slicing<kThreads>(a, slots, single_c, s_red, c, nslices, sk, tb);
 
     // XCD-aware order: workgroups are dealt to the eight XCDs round-robin by
     // id, so ids x, x + 8, x + 16, ... run on XCD x (and share its L2). The
     // (slice, row group) items, slice-major, are cut into eight contiguous
     // blocks, block x on XCD x, so the row groups of one slice run side by
     // side on one XCD and all but the first read the slice's rows from its L2
-    // (with at most 8 row groups, blocks hold whole slices).
+    // (with at most 8 row groups, blocks hold whole slices). The grid is sized
+    // for max_slices; workgroups past this batch's blocks exit here. One
+    // sequence is laid out by the host bound (its exact slice count for
+    // max_kv keys), so the mapping does not wait for seq_lens.
     const int L = blockIdx.x;
-    const int items = splits * row_groups;
+    const int items = (a.batch == 1 ? max_slices : (int)nslices) * row_groups;
     const int per_xcd = xcd_block(items, row_groups);
     const int item = (L & 7) * per_xcd + (L >> 3);
-    const int b = blockIdx.y;
     if ((L >> 3) >= per_xcd || item >= items)
-        return;  // padding of the item count to a multiple of 8
-    const int split = item / row_groups;
-    const int grp = item - split * row_groups;
+        return;  // the whole workgroup (every value above is uniform)
+    const int gslice = item / row_groups;
+    const int grp = item - gslice * row_groups;
     const int tid = threadIdx.x;
+
+    // The sequence b holding global slice gslice, its slice index there and
+    // its keys S (clamped to [N, max_kv]).
+    int b = 0;
+    int split = gslice;
+    int S = sk;
+    if (a.batch == 1 && gslice >= nslices)
+        return;  // the whole workgroup: a sequence shorter than max_kv
+    if (__builtin_expect(a.batch > 1, 0)) {
+        if (tid == 0)
+            s_hit[0] = 0, s_hit[1] = 0, s_hit[2] = 0;
+        int64_t base = 0;
+        for (int b0 = 0; b0 < a.batch; b0 += kThreads) {
+            const int bb = b0 + tid;
+            int64_t n = 0;
+            if (a.batch <= kThreads)
+                n = (tb + c - 1) / c;
+            else if (bb < a.batch)
+                n = (seq_tiles(a, bb) + c - 1) / c;
+            int64_t tot;
+            const int64_t st = base + block_excl_scan<kThreads>(n, s_red, tot);
+            if (n > 0 && gslice >= st && gslice < st + n) {
+                s_hit[0] = bb;
+                s_hit[1] = (int)(gslice - st);
+                s_hit[2] = a.batch <= kThreads ? sk : seq_keys(a, bb);
+            }
+            base += tot;
+        }
+        __syncthreads();
+        b = s_hit[0];
+        split = s_hit[1];
+        S = s_hit[2];
+    }
+    // the same values in every lane (one sequence's length, or LDS words every
+    // lane reads): keep them in scalar registers
+    b = __builtin_amdgcn_readfirstlane(b);
+    split = __builtin_amdgcn_readfirstlane(split);
+    S = __builtin_amdgcn_readfirstlane(S);
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int rl = lane & 15;   // row (and key) within a 16-block
@@ -131,11 +297,8 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(Args a, int splits, 
     const int H = a.heads;
     const int R = N * H;
 
-    const int S = min(max(a.seq_lens[b], N), a.max_kv);
-    const int k0 = split * chunk;
-    if (k0 >= S)
-        return;  // the whole workgroup: this slice lies past the sequence
-    const int nkeys = min(chunk, S - k0);
+    const int k0 = (int)((int64_t)split * c * kTileKeys);  // < S: split < ceil(tiles_b / c)
+    const int nkeys = (int)min((int64_t)S - k0, c * kTileKeys);
     const int ntiles = (nkeys + kTileKeys - 1) / kTileKeys;
 
     // Stage the slice's pool slots in windows of 128 tiles: window w (tiles
@@ -462,7 +625,7 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(Args a, int splits, 
     // Partial result of this slice, in the register-fragment order.
     float l_tot = l_run + __shfl_xor(l_run, 16);
     l_tot += __shfl_xor(l_tot, 32);
-    const size_t pidx = ((size_t)b * row_groups + grp) * splits + split;
+    const size_t pidx = (size_t)grp * max_slices + gslice;
     // O is stored rounded to bf16 (round to nearest even, relative error at
     // most 2^-8 per element); the combine scales each slice's O by a factor of
     // at most 1, so the merged output carries at most that relative error per
@@ -492,12 +655,13 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(Args a, int splits, 
 // max. The waves of a column block then merge through LDS, and the first of
 // them writes the bf16 output (16 rows x 16 columns) and, for column block 0,
 // the lse.
-__global__ __launch_bounds__(kCombineThreads) void combine_kernel(Args a, int splits, int chunk,
-                                                                   int row_groups, int wpc)
+__global__ __launch_bounds__(kCombineThreads) void combine_kernel(Args a, int slots, int single_c,
+                                                                   int max_slices, int row_groups, int wpc)
 {
     __shared__ float s_m[kCombineWaves][64];
     __shared__ float s_l[kCombineWaves][64];
     __shared__ f32x4 s_o[kCombineWaves][64];
+    __shared__ int64_t s_red[kCombineWaves];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -513,9 +677,25 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(Args a, int sp
     const int R = N * a.heads;
     const int row = grp * kRowsPerGroup + w * 16 + rl;
 
-    const int S = min(max(a.seq_lens[b], N), a.max_kv);
-    const int nvalid = min(splits, (S + chunk - 1) / chunk);
-    const size_t pbase = ((size_t)b * row_groups + grp) * splits;
+    // This sequence's slices: nvalid of them, from global slice start on.
+    int64_t c, nslices, tb;
+    int sk;
+    slicing<kCombineThreads>(a, slots, single_c, s_red, c, nslices, sk, tb);
+    int64_t start = 0;
+    int nvalid = (int)nslices;
+    if (__builtin_expect(a.batch > 1, 0)) {
+        int64_t before = 0;
+        if (a.batch <= kCombineThreads) {
+            if (tid < b)
+                before = (tb + c - 1) / c;
+        } else {
+            for (int bb = tid; bb < b; bb += kCombineThreads)
+                before += (seq_tiles(a, bb) + c - 1) / c;
+        }
+        start = block_sum<kCombineThreads>(before, s_red);
+        nvalid = (int)((seq_tiles(a, b) + c - 1) / c);
+    }
+    const size_t pbase = (size_t)grp * max_slices + (size_t)start;
     const float2* pml = (const float2*)a.part_ml + pbase * kRowsPerGroup + w * 16 + rl;
     const __bf16* pob = (const __bf16*)a.part_o + pbase * (size_t)(kRowsPerGroup * kPartRowElems) +
                         (size_t)w * (kColBlocks * 64 * 4) + (cb * 64 + lane) * 4;
@@ -595,9 +775,10 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(Args a, int sp
 hipError_t launch_split(const Plan& p, const Args& a, hipStream_t stream)
 {
     const float scale_log2 = (float)((double)a.scale * 1.4426950408889634);
-    const int per_xcd = xcd_block(p.splits * p.row_groups, p.row_groups);
-    hipLaunchKernelGGL(a.prefix_pages ? split_kernel<true> : split_kernel<false>, dim3(8 * per_xcd, a.batch), dim3(kThreads), 0,
-                       stream, a, p.splits, p.chunk, p.row_groups, scale_log2);
+    const int per_xcd = xcd_block(p.max_slices * p.row_groups, p.row_groups);
+    hipLaunchKernelGGL(a.prefix_pages ? split_kernel<true> : split_kernel<false>, dim3(8 * per_xcd),
+                       dim3(kThreads), 0, stream, a, p.slots, p.single_c, p.max_slices, p.row_groups,
+                       scale_log2);
     return hipGetLastError();
 }
 
@@ -606,10 +787,11 @@ hipError_t launch_combine(const Plan& p, const Args& a, hipStream_t stream)
     // waves per column block: enough that each loads at most kCombineUnroll
     // slices per round, at most all eight
     int wpc = 1;
-    while (wpc < kCombineWaves && wpc * kCombineUnroll < p.splits)
+    while (wpc < kCombineWaves && wpc * kCombineUnroll < p.slots)  // a sequence has <= slots slices
         wpc *= 2;
     hipLaunchKernelGGL(combine_kernel, dim3(kColBlocks * wpc / kCombineWaves, p.row_groups * 4, a.batch),
-                       dim3(kCombineThreads), 0, stream, a, p.splits, p.chunk, p.row_groups, wpc);
+                       dim3(kCombineThreads), 0, stream, a, p.slots, p.single_c, p.max_slices, p.row_groups,
+                       wpc);
     return hipGetLastError();
 }
 

@@ -184,6 +184,53 @@ def test_batch8_both_layouts(oracle_mod):
     assert np.array_equal(ga[0], gb[0]) and np.array_equal(ga[1], gb[1])
 
 
+def test_long_slices_restage_index_window(oracle_mod):
+    """Many row groups leave few, long slices: with 2048 rows over ~40k keys a
+    slice spans more than one 128-tile window of staged page indices, so the
+    kernel restages indices inside its tile loop."""
+    wl = I.make_workload(batch=1, num_nodes=64, num_heads=32, prefix_lens=[40000], num_slots=65536,
+                         tree="random", max_depth=8, config_id=107, device="cuda", q_gain=4.0)
+    plan = M.plan_query(M.make_shape(1, 64, 32, wl.max_kv, wl.num_slots), 256)
+    assert plan["chunk"] > 128 * 32, plan
+    compare(wl, oracle_mod, rows=sample_rows(wl, 64, seed=7), label="long slices")
+
+
+# ------------------------------------------------- length-balanced slicing of a batch
+
+def test_uneven_batch_balanced_slices(oracle_mod):
+    """One long sequence among short ones: the long one is cut into many
+    slices, each short one into one; every row against the oracle."""
+    wl = I.make_workload(batch=5, num_nodes=4, num_heads=4, prefix_lens=[30000, 3, 100, 0, 2500],
+                         num_slots=65536, tree="random", max_depth=3, config_id=108, device="cuda",
+                         q_gain=4.0)
+    compare(wl, oracle_mod, label="uneven batch")
+
+
+@pytest.mark.parametrize("batch", [300, 600])
+def test_many_sequences(oracle_mod, batch):
+    """More sequences than threads in a split (256) or combine (512) workgroup:
+    the slicing loops over the batch instead of one sequence per thread."""
+    rng = np.random.default_rng(batch)
+    pre = [int(x) for x in rng.integers(0, 90, size=batch)]
+    pre[batch // 2] = 4000  # one long sequence takes several slices
+    wl = I.make_workload(batch=batch, num_nodes=2, num_heads=2, prefix_lens=pre, num_slots=65536,
+                         tree="chain", config_id=109, device="cuda")
+    compare(wl, oracle_mod, label=f"{batch} sequences")
+
+
+def test_batch_slicing_is_independent_of_layout_and_padding():
+    """The slicing depends only on seq_lens: the same batch with a larger
+    max_kv (more table columns, junk past every sequence) gives the same bits."""
+    wl = I.make_workload(batch=4, num_nodes=8, num_heads=8, prefix_lens=[9000, 40, 700, 20000],
+                         num_slots=65536, tree="binary", config_id=110, device="cuda")
+    a = run_gpu(wl)
+    wide = torch.full((4, wl.max_kv + 5000), 10 ** 9, dtype=torch.int32, device="cuda")
+    wide[:, :wl.max_kv] = wl.page_table
+    wl.page_table = wide
+    b = run_gpu(wl)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1].view(np.uint32), b[1].view(np.uint32))
+
+
 # ------------------------------------------------------------------ graph capture
 
 def test_graph_capture_replays_match_eager():
