@@ -68,9 +68,12 @@ __device__ __forceinline__ void wait_vmcnt()
 #pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void gather16_to_lds(const void* src, uint32_t lds_addr)
 {
+    // lds_addr is wave-uniform by contract; readfirstlane puts it in a scalar
+    // register even where the compiler cannot prove the uniformity itself
+    const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds_addr);
     asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
                  :
-                 : "v"(src), "s"(lds_addr)
+                 : "v"(src), "s"(m0v)
                  : "memory", "m0");
 }
 #pragma clang diagnostic pop
@@ -164,12 +167,40 @@ __device__ __forceinline__ int64_t block_excl_scan(int64_t v, int64_t* red, int6
     return before + x - v;
 }
 
+// Sum over the 64 lanes of a wave; every lane gets it.
+__device__ __forceinline__ int wave_sum(int v)
+{
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1)
+        v += __shfl_xor(v, o);
+    return v;
+}
+
+// Inclusive prefix sum over the lanes of a wave.
+__device__ __forceinline__ int wave_incl_scan(int v)
+{
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(v, o);
+        if (lane >= o)
+            v += y;
+    }
+    return v;
+}
+
+// Batches of at most this many sequences are sliced by every wave on its own
+// (one sequence per lane, shuffles only: no LDS, no barrier).
+constexpr int kWaveBatch = 64;
+
 // Tiles per slice c and the number of slices of all sequences together.
 // sk and tb receive the keys and tiles of one sequence: of the batch's only
-// sequence when B = 1 (every thread), else of sequence threadIdx.x when
-// B <= NT (0 past the batch), else 0. A single sequence takes c from the host
-// (sized for max_kv, so that the grid holds exactly its slices) and needs no
-// reduction and no barrier; up to NT sequences need one load per thread.
+// sequence when B = 1 (every thread); of sequence (lane) when B <= 64 (0
+// past the batch); of sequence threadIdx.x when B <= NT (0 past the batch);
+// else 0. A single sequence takes c from the host (sized for max_kv, so that
+// the grid holds exactly its slices) and needs no reduction and no barrier;
+// up to 64 sequences need one load per lane and no barrier; up to NT one
+// load per thread.
 template <int NT>
 __device__ __forceinline__ void slicing(const Args& a, int slots, int single_c, int64_t* red,
                                         int64_t& c, int64_t& nslices, int& sk, int64_t& tb)
@@ -182,6 +213,17 @@ __device__ __forceinline__ void slicing(const Args& a, int slots, int single_c, 
         tb = t1;
         c = single_c;
         nslices = (t1 + single_c - 1) / single_c;
+        return;
+    }
+    if (B <= kWaveBatch) {
+        const int lane = threadIdx.x & 63;
+        sk = lane < B ? seq_keys(a, lane) : 0;
+        const int t1 = (sk + kTileKeys - 1) / kTileKeys;  // totals < 2^27: 32-bit
+        tb = t1;
+        const int T = wave_sum(t1);
+        const int cc = max(1, (T + target - 1) / target);
+        c = cc;
+        nslices = wave_sum((t1 + cc - 1) / cc);
         return;
     }
     int64_t t = 0;
@@ -259,7 +301,16 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(Args a, int slots, i
     int S = sk;
     if (a.batch == 1 && gslice >= nslices)
         return;  // the whole workgroup: a sequence shorter than max_kv
-    if (__builtin_expect(a.batch > 1, 0)) {
+    if (__builtin_expect(a.batch > 1 && a.batch <= kWaveBatch, 0)) {
+        // one sequence per lane: the lane whose slice range holds gslice
+        const int nl = (int)((tb + c - 1) / c);
+        const int incl = wave_incl_scan(nl);
+        const uint64_t hit = __builtin_amdgcn_ballot_w64(nl > 0 && gslice >= incl - nl && gslice < incl);
+        const int bl = __builtin_ctzll(hit);  // exactly one lane: slices are disjoint
+        b = bl;
+        split = gslice - (__shfl(incl, bl) - __shfl(nl, bl));
+        S = __shfl(sk, bl);
+    } else if (__builtin_expect(a.batch > kWaveBatch, 0)) {
         if (tid == 0)
             s_hit[0] = 0, s_hit[1] = 0, s_hit[2] = 0;
         int64_t base = 0;
@@ -297,8 +348,9 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(Args a, int slots, i
     const int H = a.heads;
     const int R = N * H;
 
-    const int k0 = (int)((int64_t)split * c * kTileKeys);  // < S: split < ceil(tiles_b / c)
-    const int nkeys = (int)min((int64_t)S - k0, c * kTileKeys);
+    // k0 < S (split < ceil(tiles_b / c)); both uniform, kept in scalar registers
+    const int k0 = __builtin_amdgcn_readfirstlane((int)((int64_t)split * c * kTileKeys));
+    const int nkeys = __builtin_amdgcn_readfirstlane((int)min((int64_t)S - k0, c * kTileKeys));
     const int ntiles = (nkeys + kTileKeys - 1) / kTileKeys;
 
     // Stage the slice's pool slots in windows of 128 tiles: window w (tiles
@@ -656,7 +708,7 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(Args a, int slots, i
 // them writes the bf16 output (16 rows x 16 columns) and, for column block 0,
 // the lse.
 __global__ __launch_bounds__(kCombineThreads) void combine_kernel(Args a, int slots, int single_c,
-                                                                   int max_slices, int row_groups, int wpc)
+                                                                   int max_slices, int row_groups)
 {
     __shared__ float s_m[kCombineWaves][64];
     __shared__ float s_l[kCombineWaves][64];
@@ -666,8 +718,6 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(Args a, int sl
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const int cb = blockIdx.x * (kCombineWaves / wpc) + wave / wpc;  // column block 0..31
-    const int sub = wave % wpc;          // this wave's share of the slices
     const int rb = blockIdx.y;           // 16-row block within the sequence
     const int b = blockIdx.z;
     const int grp = rb >> 2;
@@ -683,7 +733,12 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(Args a, int sl
     slicing<kCombineThreads>(a, slots, single_c, s_red, c, nslices, sk, tb);
     int64_t start = 0;
     int nvalid = (int)nslices;
-    if (__builtin_expect(a.batch > 1, 0)) {
+    if (__builtin_expect(a.batch > 1 && a.batch <= kWaveBatch, 0)) {
+        const int lane_b = tid & 63;  // one sequence per lane
+        const int nl = (int)((tb + c - 1) / c);
+        start = wave_sum(lane_b < b ? nl : 0);
+        nvalid = __shfl(nl, b);
+    } else if (__builtin_expect(a.batch > kWaveBatch, 0)) {
         int64_t before = 0;
         if (a.batch <= kCombineThreads) {
             if (tid < b)
@@ -695,6 +750,17 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(Args a, int sl
         start = block_sum<kCombineThreads>(before, s_red);
         nvalid = (int)((seq_tiles(a, b) + c - 1) / c);
     }
+    // Waves per column block for this sequence's slice count (1, 2, 4 or 8,
+    // at most kCombineUnroll slices each per round); the grid is sized for 8,
+    // and workgroups this sequence does not need exit here.
+    nvalid = __builtin_amdgcn_readfirstlane(nvalid);
+    int wpc = 1;
+    while (wpc < kCombineWaves && wpc * kCombineUnroll < nvalid)
+        wpc *= 2;
+    if ((int)blockIdx.x >= kColBlocks * wpc / kCombineWaves)
+        return;  // the whole workgroup (uniform)
+    const int cb = blockIdx.x * (kCombineWaves / wpc) + wave / wpc;  // column block 0..31
+    const int sub = wave % wpc;          // this wave's share of the slices
     const size_t pbase = (size_t)grp * max_slices + (size_t)start;
     const float2* pml = (const float2*)a.part_ml + pbase * kRowsPerGroup + w * 16 + rl;
     const __bf16* pob = (const __bf16*)a.part_o + pbase * (size_t)(kRowsPerGroup * kPartRowElems) +
@@ -784,14 +850,13 @@ hipError_t launch_split(const Plan& p, const Args& a, hipStream_t stream)
 
 hipError_t launch_combine(const Plan& p, const Args& a, hipStream_t stream)
 {
-    // waves per column block: enough that each loads at most kCombineUnroll
-    // slices per round, at most all eight
+    // grid for the most waves per column block a sequence can need (it has at
+    // most `slots` slices); each workgroup picks its sequence's own count
     int wpc = 1;
-    while (wpc < kCombineWaves && wpc * kCombineUnroll < p.slots)  // a sequence has <= slots slices
+    while (wpc < kCombineWaves && wpc * kCombineUnroll < p.slots)
         wpc *= 2;
     hipLaunchKernelGGL(combine_kernel, dim3(kColBlocks * wpc / kCombineWaves, p.row_groups * 4, a.batch),
-                       dim3(kCombineThreads), 0, stream, a, p.slots, p.single_c, p.max_slices, p.row_groups,
-                       wpc);
+                       dim3(kCombineThreads), 0, stream, a, p.slots, p.single_c, p.max_slices, p.row_groups);
     return hipGetLastError();
 }
 
