@@ -105,8 +105,9 @@ size_t mla_tree_verify_workspace_size(const mtv_shape* shape);
  *   out        bf16 [B][N][H][512]  written in full (round to nearest even)
  *   lse        fp32 [B][N][H]       natural-log sum of exp(scaled scores)
  *   workspace  >= mla_tree_verify_workspace_size(shape) bytes, 256-byte aligned;
- *              scratch for per-slice partial results. Its contents need no
- *              initialisation and are meaningless after the call.
+ *              scratch for per-slice partial results and each sequence's
+ *              slice range. Its contents need no initialisation and are
+ *              meaningless after the call.
  *
  * Outputs must not alias inputs or the workspace. Calls that share a workspace
  * must be ordered on one stream.
@@ -181,7 +182,8 @@ int mla_tree_verify_paged(const mtv_shape* shape,
  * inputs as mla_tree_verify and leaves, in `workspace`, one partial per
  * (64-row group, key slice of the batch): the unnormalised weighted latent sum
  * (stored as bf16, 1024 B per row), the running max of the scaled scores in
- * log2 units and the sum of 2^(score*log2(e) - max) (fp32, 8 B per row).
+ * log2 units and the sum of 2^(score*log2(e) - max) (fp32, 8 B per row),
+ * and, per sequence, its first batch slice and slice count (two int32).
  * mla_tree_verify_combine merges those partials by
  * log-sum-exp and writes out and lse. The combine must run on a workspace
  * filled by a splitkv call with the same shape, seq_lens and device, ordered

@@ -83,7 +83,8 @@ mtv::Plan make_plan(const mtv_shape& s, int cus)
     const size_t parts = (size_t)p.row_groups * (size_t)p.max_slices;
     p.part_o_off = 0;
     p.part_ml_off = align_up(parts * mtv::kRowsPerGroup * mtv::kDv * sizeof(uint16_t), 256);
-    p.bytes = align_up(p.part_ml_off + parts * mtv::kRowsPerGroup * 2 * sizeof(float), 256);
+    p.seq_off = align_up(p.part_ml_off + parts * mtv::kRowsPerGroup * 2 * sizeof(float), 256);
+    p.bytes = align_up(p.seq_off + (size_t)s.batch * 2 * sizeof(int32_t), 256);
     return p;
 }
 
@@ -181,6 +182,7 @@ int run(int phases, const mtv_shape* shape, const void* q, const void* kv_pool,
     a.lse = lse;
     a.part_o = (uint16_t*)((char*)workspace + plan.part_o_off);
     a.part_ml = (float*)((char*)workspace + plan.part_ml_off);
+    a.seq_slices = (int32_t*)((char*)workspace + plan.seq_off);
     a.batch = shape->batch;
     a.nodes = shape->num_nodes;
     a.heads = shape->num_heads;

@@ -24,7 +24,7 @@ struct Plan {
     int single_c;      // tiles per slice of a batch of one sequence (from max_kv)
     int splits;        // slices per sequence when every sequence holds max_kv keys
     int chunk;         // keys per slice in that case, a multiple of kTileKeys
-    size_t part_o_off, part_ml_off, bytes;  // workspace layout
+    size_t part_o_off, part_ml_off, seq_off, bytes;  // workspace layout
 };
 
 struct Args {
@@ -36,8 +36,9 @@ struct Args {
     float scale;
     void* out;
     float* lse;
-    uint16_t* part_o;  // bf16 [B][G][splits][64 rows as 4 waves x 32 col-blocks x 64 lanes x 4]
-    float* part_ml;  // [B][G][splits][64 rows][2]  (running max in log2 units, sum)
+    uint16_t* part_o;  // bf16 [row group][batch slice][64 rows as 4 waves x 32 col-blocks x 64 lanes x 4]
+    float* part_ml;    // [row group][batch slice][64 rows][2]  (running max in log2 units, sum)
+    int32_t* seq_slices;  // [B][2]: first batch slice and slice count of each sequence
     int batch, nodes, heads, max_kv;
     int64_t num_slots;
     // hybrid paging (NULL prefix_pages: the per-token page_table is used)

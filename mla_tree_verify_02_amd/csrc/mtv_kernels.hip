@@ -348,6 +348,13 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(Args a, int slots, i
     const int H = a.heads;
     const int R = N * H;
 
+    // The workgroup of a sequence's first slice (row group 0) records where the
+    // sequence's slices start and how many there are, for the combine.
+    if (split == 0 && grp == 0 && tid == 0) {
+        const int tiles_b = (S + kTileKeys - 1) / kTileKeys;
+        a.seq_slices[2 * b] = gslice;
+        a.seq_slices[2 * b + 1] = (int)((tiles_b + c - 1) / c);
+    }
     // k0 < S (split < ceil(tiles_b / c)); both uniform, kept in scalar registers
     const int k0 = __builtin_amdgcn_readfirstlane((int)((int64_t)split * c * kTileKeys));
     const int nkeys = __builtin_amdgcn_readfirstlane((int)min((int64_t)S - k0, c * kTileKeys));
@@ -707,13 +714,12 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(Args a, int slots, i
 // max. The waves of a column block then merge through LDS, and the first of
 // them writes the bf16 output (16 rows x 16 columns) and, for column block 0,
 // the lse.
-__global__ __launch_bounds__(kCombineThreads) void combine_kernel(Args a, int slots, int single_c,
-                                                                   int max_slices, int row_groups)
+__global__ __launch_bounds__(kCombineThreads) void combine_kernel(Args a, int single_c, int max_slices,
+                                                                   int row_groups)
 {
     __shared__ float s_m[kCombineWaves][64];
     __shared__ float s_l[kCombineWaves][64];
     __shared__ f32x4 s_o[kCombineWaves][64];
-    __shared__ int64_t s_red[kCombineWaves];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -727,28 +733,17 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(Args a, int sl
     const int R = N * a.heads;
     const int row = grp * kRowsPerGroup + w * 16 + rl;
 
-    // This sequence's slices: nvalid of them, from global slice start on.
-    int64_t c, nslices, tb;
-    int sk;
-    slicing<kCombineThreads>(a, slots, single_c, s_red, c, nslices, sk, tb);
+    // This sequence's slices: nvalid of them, from batch slice start on. One
+    // sequence has the host's slicing; in a batch, the split kernel recorded
+    // each sequence's range in the workspace.
     int64_t start = 0;
-    int nvalid = (int)nslices;
-    if (__builtin_expect(a.batch > 1 && a.batch <= kWaveBatch, 0)) {
-        const int lane_b = tid & 63;  // one sequence per lane
-        const int nl = (int)((tb + c - 1) / c);
-        start = wave_sum(lane_b < b ? nl : 0);
-        nvalid = __shfl(nl, b);
-    } else if (__builtin_expect(a.batch > kWaveBatch, 0)) {
-        int64_t before = 0;
-        if (a.batch <= kCombineThreads) {
-            if (tid < b)
-                before = (tb + c - 1) / c;
-        } else {
-            for (int bb = tid; bb < b; bb += kCombineThreads)
-                before += (seq_tiles(a, bb) + c - 1) / c;
-        }
-        start = block_sum<kCombineThreads>(before, s_red);
-        nvalid = (int)((seq_tiles(a, b) + c - 1) / c);
+    int nvalid;
+    if (a.batch == 1) {
+        const int t1 = (seq_keys(a, 0) + kTileKeys - 1) / kTileKeys;
+        nvalid = (t1 + single_c - 1) / single_c;
+    } else {
+        start = a.seq_slices[2 * b];
+        nvalid = a.seq_slices[2 * b + 1];
     }
     // Waves per column block for this sequence's slice count (1, 2, 4 or 8,
     // at most kCombineUnroll slices each per round); the grid is sized for 8,
@@ -856,7 +851,7 @@ hipError_t launch_combine(const Plan& p, const Args& a, hipStream_t stream)
     while (wpc < kCombineWaves && wpc * kCombineUnroll < p.slots)
         wpc *= 2;
     hipLaunchKernelGGL(combine_kernel, dim3(kColBlocks * wpc / kCombineWaves, p.row_groups * 4, a.batch),
-                       dim3(kCombineThreads), 0, stream, a, p.slots, p.single_c, p.max_slices, p.row_groups);
+                       dim3(kCombineThreads), 0, stream, a, p.single_c, p.max_slices, p.row_groups);
     return hipGetLastError();
 }
 
