@@ -44,7 +44,6 @@ constexpr int kPartRowElems = kDv;                               // bf16 element
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kCombineWaves = 8;                                 // waves per combine workgroup
 constexpr int kCombineThreads = kCombineWaves * 64;
-constexpr int kCombineUnroll = 16;                               // slices in flight per wave
 
 static_assert(kKeysPerWave * kChunks % 64 == 0, "tile rows must fill whole wave loads");
 static_assert(kTileKeys == 32, "the P.V k-step covers exactly one tile");
@@ -706,20 +705,27 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(Args a, int slots, i
     }
 }
 
-// One workgroup of 8 waves per (sequence, 16-row block, group of 8/wpc
-// 16-column blocks): `wpc` waves share each column block (1, 2, 4 or 8, chosen
-// by the host from the slice count). A wave takes every wpc-th slice of its
-// column block, loads kCombineUnroll of them at once and folds them into its
-// running (max, sum, weighted sum) with one exp per slice against the round's
-// max. The waves of a column block then merge through LDS, and the first of
-// them writes the bf16 output (16 rows x 16 columns) and, for column block 0,
-// the lse.
+// One workgroup of 8 waves per (sequence, 16-row block, group of column
+// units). A unit is a 16-column block (kVals = 4: a lane holds the 4 values of
+// one fragment lane) or half of one (kVals = 2: 8 columns, 2 values per lane,
+// twice the waves for the same data; used for one sequence with many slices,
+// where the slices rather than the rows are the work). `wpc` waves share each
+// unit (1, 2, 4 or 8, from the sequence's slice count). A wave takes every
+// wpc-th slice, loads kUnroll of them at once and folds them into its running
+// (max, sum, weighted sum) with one exp per slice against the round's max. The
+// waves of a unit then merge through LDS, and the first of them writes the
+// bf16 output and, for column block 0, the lse.
+template <int kVals>
 __global__ __launch_bounds__(kCombineThreads) void combine_kernel(Args a, int single_c, int max_slices,
                                                                    int row_groups)
 {
+    constexpr int kUnroll = kVals == 2 ? 32 : 16;   // slices in flight per wave
+    constexpr int kUnits = kColBlocks * 4 / kVals;  // units per 16-row block
+    typedef float fvec __attribute__((ext_vector_type(kVals)));
+    typedef __bf16 bvec __attribute__((ext_vector_type(kVals)));
     __shared__ float s_m[kCombineWaves][64];
     __shared__ float s_l[kCombineWaves][64];
-    __shared__ f32x4 s_o[kCombineWaves][64];
+    __shared__ fvec s_o[kCombineWaves][64];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -728,10 +734,8 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(Args a, int si
     const int b = blockIdx.z;
     const int grp = rb >> 2;
     const int w = rb & 3;
-    const int rl = lane & 15;
     const int N = a.nodes;
     const int R = N * a.heads;
-    const int row = grp * kRowsPerGroup + w * 16 + rl;
 
     // This sequence's slices: nvalid of them, from batch slice start on. One
     // sequence has the host's slicing; in a batch, the split kernel recorded
@@ -745,58 +749,63 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(Args a, int si
         start = a.seq_slices[2 * b];
         nvalid = a.seq_slices[2 * b + 1];
     }
-    // Waves per column block for this sequence's slice count (1, 2, 4 or 8,
-    // at most kCombineUnroll slices each per round); the grid is sized for 8,
-    // and workgroups this sequence does not need exit here.
+    // Waves per unit for this sequence's slice count; the grid is sized for
+    // the most a sequence can need, and workgroups this one does not need
+    // exit here.
     nvalid = __builtin_amdgcn_readfirstlane(nvalid);
     int wpc = 1;
-    while (wpc < kCombineWaves && wpc * kCombineUnroll < nvalid)
+    while (wpc < kCombineWaves && wpc * kUnroll < nvalid)
         wpc *= 2;
-    if ((int)blockIdx.x >= kColBlocks * wpc / kCombineWaves)
+    if ((int)blockIdx.x >= kUnits * wpc / kCombineWaves)
         return;  // the whole workgroup (uniform)
-    const int cb = blockIdx.x * (kCombineWaves / wpc) + wave / wpc;  // column block 0..31
+    const int unit = blockIdx.x * (kCombineWaves / wpc) + wave / wpc;
     const int sub = wave % wpc;          // this wave's share of the slices
+    // column block, fragment lane of the split kernel's O^T layout, and the
+    // first of this lane's values in it
+    const int cb = kVals == 4 ? unit : unit >> 1;
+    const int fl = kVals == 4 ? lane : 32 * (unit & 1) + (lane >> 1);
+    const int v0 = kVals == 4 ? 0 : 2 * (lane & 1);
+    const int rl = fl & 15;
+    const int row = grp * kRowsPerGroup + w * 16 + rl;
+
     const size_t pbase = (size_t)grp * max_slices + (size_t)start;
     const float2* pml = (const float2*)a.part_ml + pbase * kRowsPerGroup + w * 16 + rl;
     const __bf16* pob = (const __bf16*)a.part_o + pbase * (size_t)(kRowsPerGroup * kPartRowElems) +
-                        (size_t)w * (kColBlocks * 64 * 4) + (cb * 64 + lane) * 4;
+                        (size_t)w * (kColBlocks * 64 * 4) + (cb * 64 + fl) * 4 + v0;
 
     float M = -INFINITY;
     float L = 0.f;
-    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int s0 = sub; s0 < nvalid; s0 += wpc * kCombineUnroll) {
-        float2 ml[kCombineUnroll];
-        f32x4 o[kCombineUnroll];
+    fvec acc = fvec{};
+    for (int s0 = sub; s0 < nvalid; s0 += wpc * kUnroll) {
+        float2 ml[kUnroll];
+        bvec ov[kUnroll];
 #pragma unroll
-        for (int u = 0; u < kCombineUnroll; ++u) {
+        for (int u = 0; u < kUnroll; ++u) {
             const int s = s0 + u * wpc;
-            const bool in = s < nvalid;
-            const size_t ss = in ? (size_t)s : 0;
+            const size_t ss = s < nvalid ? (size_t)s : 0;
             ml[u] = pml[ss * kRowsPerGroup];
-            const bf16x4 v = *(const bf16x4*)(pob + ss * (kRowsPerGroup * kPartRowElems));
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                o[u][i] = (float)v[i];
-            if (!in) {
-                ml[u] = make_float2(-INFINITY, 0.f);
-                o[u] = f32x4{0.f, 0.f, 0.f, 0.f};
-            }
+            ov[u] = *(const bvec*)(pob + ss * (kRowsPerGroup * kPartRowElems));
         }
         float mx = M;
 #pragma unroll
-        for (int u = 0; u < kCombineUnroll; ++u)
+        for (int u = 0; u < kUnroll; ++u) {
+            if (s0 + u * wpc >= nvalid)
+                ml[u] = make_float2(-INFINITY, 0.f);  // past the sequence: weight 0
             mx = fmaxf(mx, ml[u].x);
+        }
         if (mx == -INFINITY)
             continue;  // nothing visible to this row so far
         const float ca = exp2f(M - mx);  // 0 while M is still -inf
         L *= ca;
         acc *= ca;
 #pragma unroll
-        for (int u = 0; u < kCombineUnroll; ++u) {
+        for (int u = 0; u < kUnroll; ++u) {
             // a slice that saw nothing has (m, l, o) = (-inf, 0, 0): weight 0
             const float cs = exp2f(ml[u].x - mx);
             L += ml[u].y * cs;
-            acc += o[u] * cs;
+#pragma unroll
+            for (int i = 0; i < kVals; ++i)
+                acc[i] += (float)ov[u][i] * cs;
         }
         M = mx;
     }
@@ -811,7 +820,7 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(Args a, int si
         Mt = fmaxf(Mt, s_m[wave + k][lane]);
     const float mref = (Mt == -INFINITY) ? 0.f : Mt;
     float Lt = 0.f;
-    f32x4 ot = f32x4{0.f, 0.f, 0.f, 0.f};
+    fvec ot = fvec{};
     for (int k = 0; k < wpc; ++k) {
         const float c = exp2f(s_m[wave + k][lane] - mref);  // 0 for waves that saw nothing
         Lt += s_l[wave + k][lane] * c;
@@ -820,14 +829,13 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(Args a, int si
     if (row >= R)
         return;
     const float inv = Lt > 0.f ? 1.f / Lt : 0.f;
-    bf16x4 v;
-    v[0] = (__bf16)(ot[0] * inv);
-    v[1] = (__bf16)(ot[1] * inv);
-    v[2] = (__bf16)(ot[2] * inv);
-    v[3] = (__bf16)(ot[3] * inv);
+    bvec v;
+#pragma unroll
+    for (int i = 0; i < kVals; ++i)
+        v[i] = (__bf16)(ot[i] * inv);
     __bf16* orow = (__bf16*)a.out + ((size_t)b * R + row) * kDv;
-    *(bf16x4*)(orow + 16 * cb + 4 * (lane >> 4)) = v;
-    if (cb == 0 && lane < 16)
+    *(bvec*)(orow + 16 * cb + 4 * (fl >> 4) + v0) = v;
+    if (cb == 0 && fl < 16 && v0 == 0)
         a.lse[(size_t)b * R + row] = Lt > 0.f ? (Mt + log2f(Lt)) * kLn2 : -INFINITY;
 }
 
@@ -845,13 +853,19 @@ hipError_t launch_split(const Plan& p, const Args& a, hipStream_t stream)
 
 hipError_t launch_combine(const Plan& p, const Args& a, hipStream_t stream)
 {
-    // grid for the most waves per column block a sequence can need (it has at
-    // most `slots` slices); each workgroup picks its sequence's own count
+    // One sequence with many slices: half column blocks (twice the waves, 32
+    // slices in flight each); otherwise whole column blocks (16 in flight).
+    // The grid is sized for the most waves per unit a sequence can need (it
+    // has at most `slots` slices); each workgroup picks its sequence's count.
+    const bool half = a.batch == 1 && p.splits > 32;
+    const int unroll = half ? 32 : 16;
+    const int units = half ? 2 * kColBlocks : kColBlocks;
     int wpc = 1;
-    while (wpc < kCombineWaves && wpc * kCombineUnroll < p.slots)
+    while (wpc < kCombineWaves && wpc * unroll < p.slots)
         wpc *= 2;
-    hipLaunchKernelGGL(combine_kernel, dim3(kColBlocks * wpc / kCombineWaves, p.row_groups * 4, a.batch),
-                       dim3(kCombineThreads), 0, stream, a, p.single_c, p.max_slices, p.row_groups);
+    hipLaunchKernelGGL(half ? combine_kernel<2> : combine_kernel<4>,
+                       dim3(units * wpc / kCombineWaves, p.row_groups * 4, a.batch), dim3(kCombineThreads), 0,
+                       stream, a, p.single_c, p.max_slices, p.row_groups);
     return hipGetLastError();
 }
 
