@@ -206,10 +206,11 @@ def test_uneven_batch_balanced_slices(oracle_mod):
     compare(wl, oracle_mod, label="uneven batch")
 
 
-@pytest.mark.parametrize("batch", [300, 600])
+@pytest.mark.parametrize("batch", [64, 65, 100, 256, 300, 600])
 def test_many_sequences(oracle_mod, batch):
-    """More sequences than threads in a split (256) or combine (512) workgroup:
-    the slicing loops over the batch instead of one sequence per thread."""
+    """The edges of the slicing paths: one sequence per lane up to 64, then
+    the split kernel's block-wide slicing, with one sequence per thread up to
+    256 and a loop over the batch beyond."""
     rng = np.random.default_rng(batch)
     pre = [int(x) for x in rng.integers(0, 90, size=batch)]
     pre[batch // 2] = 4000  # one long sequence takes several slices
