@@ -12,6 +12,8 @@
 //   only to the tree block ("The Moment of Certainty", The Path Forward; "The
 //   GPU That Wasn't There", The Native Engine Thesis): here the mask test runs
 //   only in tiles that reach the tree block or the end of the sequence.
+//   Slices have one length for the whole batch, derived on the device from
+//   seq_lens (slicing()), so a long sequence gets many and a short one few.
 // combine_kernel: merges the slices of each row by log-sum-exp and writes the
 //   bf16 output and the natural-log lse.
 #include <hip/hip_runtime.h>
