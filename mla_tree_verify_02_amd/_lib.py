@@ -94,6 +94,8 @@ def workspace_size(shape: MtvShape) -> int:
 
 
 def plan_query(shape: MtvShape, num_cus: int):
+    """The slicing mtv_plan_query reports for a batch whose sequences all hold
+    max_kv keys: slices per sequence, keys per slice, 64-row groups."""
     s, c, g = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
     rc = load().mtv_plan_query(ctypes.byref(shape), int(num_cus), ctypes.byref(s),
                                ctypes.byref(c), ctypes.byref(g))
