@@ -680,8 +680,6 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(Args a, int slots, i
             o[cb] *= alpha;
     }
 
-    wait_vmcnt<0>();  // the last tiles' loads land before the workgroup ends
-
     // Partial result of this slice, in the register-fragment order.
     float l_tot = l_run + __shfl_xor(l_run, 16);
     l_tot += __shfl_xor(l_tot, 32);
@@ -690,7 +688,9 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(Args a, int slots, i
     // most 2^-8 per element); the combine scales each slice's O by a factor of
     // at most 1, so the merged output carries at most that relative error per
     // slice term. It halves the partial traffic; the running max and sum stay
-    // fp32, so the lse is unaffected.
+    // fp32, so the lse is unaffected. The stores are non-temporal (read once,
+    // by the combine) and go out before the wait for the last prefetch
+    // gathers, so that the two latencies overlap.
     __bf16* po = (__bf16*)a.part_o + pidx * (size_t)(kRowsPerGroup * kPartRowElems) +
                  (size_t)wave * (kColBlocks * 64 * 4);
 #pragma unroll
@@ -699,12 +699,13 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(Args a, int slots, i
 #pragma unroll
         for (int i = 0; i < 4; ++i)
             v[i] = (__bf16)o[cb][i];
-        *(bf16x4*)(po + (cb * 64 + lane) * 4) = v;
+        __builtin_nontemporal_store(v, (bf16x4*)(po + (cb * 64 + lane) * 4));
     }
     if (lg == 0) {
         float2* pm = (float2*)a.part_ml + pidx * kRowsPerGroup + wave * 16 + rl;
         *pm = make_float2(m_ref, l_tot);
     }
+    wait_vmcnt<0>();  // the last gathers land before the workgroup ends
 }
 
 // One workgroup of 8 waves per (sequence, 16-row block, group of column
