@@ -77,6 +77,16 @@ __device__ __forceinline__ void gather16_to_lds(const void* src, uint32_t lds_ad
                  : "v"(src), "s"(m0v)
                  : "memory", "m0");
 }
+
+// The same for one 4-byte word per lane: lane i's word lands at lds_addr + 4 * i.
+__device__ __forceinline__ void gather4_to_lds(const void* src, uint32_t lds_addr)
+{
+    const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds_addr);
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
+                 :
+                 : "v"(src), "s"(m0v)
+                 : "memory", "m0");
+}
 #pragma clang diagnostic pop
 
 // Chunk permutation of tile row `key`: physical 16-byte slot of logical chunk c
@@ -388,9 +398,20 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(Args a, int slots, i
     };
     auto stage = [&](int w) {
         const int n = min(ntiles * kTileKeys - w * kWinKeys, kWinKeys);
-        int* dst = s_idx[w & 1];
-        for (int i = tid; i < n; i += kThreads)
-            dst[i] = slot_of(min(k0 + w * kWinKeys + i, S - 1));
+        if constexpr (kPaged) {
+            int* dst = s_idx[w & 1];
+            for (int i = tid; i < n; i += kThreads)
+                dst[i] = slot_of(min(k0 + w * kWinKeys + i, S - 1));
+        } else {
+            // Table words go straight to LDS (direct loads, no registers and
+            // no wait here): the vmcnt waits of the tile loop, which only
+            // follow later loads, cover them, and the barriers publish them.
+            // The position is clamped in the address; the slot value when a
+            // lane reads it (load_idx).
+            const uint32_t dst = (uint32_t)(uintptr_t)(LDS_AS int*)s_idx[w & 1] + wave * 256;
+            for (int i = 0; i < n; i += kThreads)
+                gather4_to_lds(pt + min(k0 + w * kWinKeys + i + tid, S - 1), dst + i * 4);
+        }
     };
     stage(0);
 
@@ -436,7 +457,7 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(Args a, int slots, i
         const int* tidx = &s_idx[(t / kWinTiles) & 1][(t % kWinTiles) * kTileKeys + wave * kKeysPerWave];
 #pragma unroll
         for (int j = 0; j < kLoadsPerWave; ++j)
-            out[j] = tidx[gkl[j]];
+            out[j] = min(max(tidx[gkl[j]], 0), maxslot);  // slots clamped to the pool
     };
     auto issue = [&](int t, const int* idx) {
         const uint32_t dst = lds0 + (uint32_t)((t % kStages) * kTileBytes +
