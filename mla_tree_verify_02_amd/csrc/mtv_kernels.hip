@@ -709,9 +709,11 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(Args a, int slots, i
     // most 2^-8 per element); the combine scales each slice's O by a factor of
     // at most 1, so the merged output carries at most that relative error per
     // slice term. It halves the partial traffic; the running max and sum stay
-    // fp32, so the lse is unaffected. The stores are non-temporal (read once,
-    // by the combine) and go out before the wait for the last prefetch
-    // gathers, so that the two latencies overlap.
+    // fp32, so the lse is unaffected. The stores are device-scope: written
+    // through this XCD's L2 (the combine runs on every XCD and reads past
+    // it), so the end of the kernel has no dirty lines to write back. They go
+    // out before the wait for the last prefetch gathers, so that the two
+    // latencies overlap.
     __bf16* po = (__bf16*)a.part_o + pidx * (size_t)(kRowsPerGroup * kPartRowElems) +
                  (size_t)wave * (kColBlocks * 64 * 4);
 #pragma unroll
@@ -720,11 +722,13 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(Args a, int slots, i
 #pragma unroll
         for (int i = 0; i < 4; ++i)
             v[i] = (__bf16)o[cb][i];
-        __builtin_nontemporal_store(v, (bf16x4*)(po + (cb * 64 + lane) * 4));
+        __hip_atomic_store((uint64_t*)(po + (cb * 64 + lane) * 4), __builtin_bit_cast(uint64_t, v),
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     if (lg == 0) {
         float2* pm = (float2*)a.part_ml + pidx * kRowsPerGroup + wave * 16 + rl;
-        *pm = make_float2(m_ref, l_tot);
+        __hip_atomic_store((uint64_t*)pm, __builtin_bit_cast(uint64_t, make_float2(m_ref, l_tot)),
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     wait_vmcnt<0>();  // the last gathers land before the workgroup ends
 }
