@@ -730,7 +730,12 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(Args a, int slots, i
         __hip_atomic_store((uint64_t*)pm, __builtin_bit_cast(uint64_t, make_float2(m_ref, l_tot)),
                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-    wait_vmcnt<0>();  // the last gathers land before the workgroup ends
+    // The last prefetch gathers write LDS, so they must land before the
+    // workgroup ends. The 32 stores of O above are younger than every
+    // gather and are always issued, and vmcnt retires in order: at most 32
+    // outstanding operations means every gather has landed, without waiting
+    // for the stores.
+    wait_vmcnt<kColBlocks>();
 }
 
 // One workgroup of 8 waves per (sequence, 16-row block, group of column
