@@ -59,6 +59,7 @@ mtv::Plan make_plan(const mtv_shape& s, int cus)
 {
     mtv::Plan p{};
     p.rows = s.num_nodes * s.num_heads;
+    p.cus = cus;
     p.row_groups = (p.rows + mtv::kRowsPerGroup - 1) / mtv::kRowsPerGroup;
     int64_t slots = ((int64_t)cus + p.row_groups - 1) / p.row_groups;
     if (slots < 1)

@@ -18,6 +18,7 @@ constexpr int kRowsPerGroup = 64;  // query rows per split workgroup (4 waves x 
 // How one call is cut into workgroups. Depends only on host values.
 struct Plan {
     int rows;          // R = N * H query rows per sequence
+    int cus;           // compute units of the device the plan is for
     int row_groups;    // ceil(R / 64)
     int slots;         // G: target key slices per row group over the whole batch
     int max_slices;    // G + B: bound on the slices of all sequences together

@@ -738,60 +738,40 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(Args a, int slots, i
     wait_vmcnt<kColBlocks>();
 }
 
-// One workgroup of 8 waves per (sequence, 16-row block, group of column
-// units). A unit is a 16-column block (kVals = 4: a lane holds the 4 values of
-// one fragment lane) or half of one (kVals = 2: 8 columns, 2 values per lane,
-// twice the waves for the same data; used for one sequence with many slices,
-// where the slices rather than the rows are the work). `wpc` waves share each
-// unit (1, 2, 4 or 8, from the sequence's slice count). A wave takes every
-// wpc-th slice, loads kUnroll of them at once and folds them into its running
-// (max, sum, weighted sum) with one exp per slice against the round's max. The
-// waves of a unit then merge through LDS, and the first of them writes the
-// bf16 output and, for column block 0, the lse.
+// Merge of one (sequence b, 16-row block rb, group xblk of column units) by
+// the workgroup's 8 waves. A unit is a 16-column block (kVals = 4: a lane
+// holds the 4 values of one fragment lane) or half of one (kVals = 2: 8
+// columns, 2 values per lane, twice the waves for the same data; used for one
+// sequence with many slices, where the slices rather than the rows are the
+// work). `wpc` waves share each unit (1, 2, 4 or 8, from the sequence's slice
+// count). A wave takes every wpc-th of the sequence's nvalid slices (from
+// batch slice `start` on), loads kUnroll of them at once and folds them into
+// its running (max, sum, weighted sum) with one exp per slice against the
+// round's max. The waves of a unit then merge through LDS, and the first of
+// them writes the bf16 output and, for column block 0, the lse. Every wave
+// passes the one barrier inside.
 template <int kVals>
-__global__ __launch_bounds__(kCombineThreads) void combine_kernel(Args a, int single_c, int max_slices,
-                                                                   int row_groups)
+struct CombineSmem {
+    typedef float fvec __attribute__((ext_vector_type(kVals)));
+    float m[kCombineWaves][64];
+    float l[kCombineWaves][64];
+    fvec o[kCombineWaves][64];
+};
+
+template <int kVals>
+__device__ __forceinline__ void combine_unit(const Args& a, CombineSmem<kVals>& sm, int b, int rb, int xblk,
+                                             int64_t start, int nvalid, int wpc, int max_slices)
 {
     constexpr int kUnroll = kVals == 2 ? 32 : 16;   // slices in flight per wave
-    constexpr int kUnits = kColBlocks * 4 / kVals;  // units per 16-row block
     typedef float fvec __attribute__((ext_vector_type(kVals)));
     typedef __bf16 bvec __attribute__((ext_vector_type(kVals)));
-    __shared__ float s_m[kCombineWaves][64];
-    __shared__ float s_l[kCombineWaves][64];
-    __shared__ fvec s_o[kCombineWaves][64];
-
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const int rb = blockIdx.y;           // 16-row block within the sequence
-    const int b = blockIdx.z;
     const int grp = rb >> 2;
     const int w = rb & 3;
-    const int N = a.nodes;
-    const int R = N * a.heads;
-
-    // This sequence's slices: nvalid of them, from batch slice start on. One
-    // sequence has the host's slicing; in a batch, the split kernel recorded
-    // each sequence's range in the workspace.
-    int64_t start = 0;
-    int nvalid;
-    if (a.batch == 1) {
-        const int t1 = (seq_keys(a, 0) + kTileKeys - 1) / kTileKeys;
-        nvalid = (t1 + single_c - 1) / single_c;
-    } else {
-        start = a.seq_slices[2 * b];
-        nvalid = a.seq_slices[2 * b + 1];
-    }
-    // Waves per unit for this sequence's slice count; the grid is sized for
-    // the most a sequence can need, and workgroups this one does not need
-    // exit here.
-    nvalid = __builtin_amdgcn_readfirstlane(nvalid);
-    int wpc = 1;
-    while (wpc < kCombineWaves && wpc * kUnroll < nvalid)
-        wpc *= 2;
-    if ((int)blockIdx.x >= kUnits * wpc / kCombineWaves)
-        return;  // the whole workgroup (uniform)
-    const int unit = blockIdx.x * (kCombineWaves / wpc) + wave / wpc;
+    const int R = a.nodes * a.heads;
+    const int unit = xblk * (kCombineWaves / wpc) + wave / wpc;
     const int sub = wave % wpc;          // this wave's share of the slices
     // column block, fragment lane of the split kernel's O^T layout, and the
     // first of this lane's values in it
@@ -842,22 +822,22 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(Args a, int si
         }
         M = mx;
     }
-    s_m[wave][lane] = M;
-    s_l[wave][lane] = L;
-    s_o[wave][lane] = acc;
+    sm.m[wave][lane] = M;
+    sm.l[wave][lane] = L;
+    sm.o[wave][lane] = acc;
     __syncthreads();
     if (sub != 0)
         return;
-    float Mt = s_m[wave][lane];
+    float Mt = sm.m[wave][lane];
     for (int k = 1; k < wpc; ++k)
-        Mt = fmaxf(Mt, s_m[wave + k][lane]);
+        Mt = fmaxf(Mt, sm.m[wave + k][lane]);
     const float mref = (Mt == -INFINITY) ? 0.f : Mt;
     float Lt = 0.f;
     fvec ot = fvec{};
     for (int k = 0; k < wpc; ++k) {
-        const float c = exp2f(s_m[wave + k][lane] - mref);  // 0 for waves that saw nothing
-        Lt += s_l[wave + k][lane] * c;
-        ot += s_o[wave + k][lane] * c;
+        const float c = exp2f(sm.m[wave + k][lane] - mref);  // 0 for waves that saw nothing
+        Lt += sm.l[wave + k][lane] * c;
+        ot += sm.o[wave + k][lane] * c;
     }
     if (row >= R)
         return;
@@ -870,6 +850,78 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(Args a, int si
     *(bvec*)(orow + 16 * cb + 4 * (fl >> 4) + v0) = v;
     if (cb == 0 && fl < 16 && v0 == 0)
         a.lse[(size_t)b * R + row] = Lt > 0.f ? (Mt + log2f(Lt)) * kLn2 : -INFINITY;
+}
+
+// Waves per column unit for a sequence of nvalid slices: enough that a wave
+// loads at most one round of slices.
+template <int kVals>
+__device__ __forceinline__ int combine_wpc(int nvalid)
+{
+    constexpr int kUnroll = kVals == 2 ? 32 : 16;
+    int wpc = 1;
+    while (wpc < kCombineWaves && wpc * kUnroll < nvalid)
+        wpc *= 2;
+    return wpc;
+}
+
+// kLoop = false: one workgroup per (sequence, 16-row block, group of column
+// units); the grid is sized for the most waves per unit a sequence can need,
+// and workgroups a sequence does not need exit at once.
+// kLoop = true (batches of 2..64 sequences): a fixed grid whose workgroups
+// walk the (sequence, 16-row block, group) items the batch actually needs,
+// numbered sequence by sequence. Every workgroup derives the count of each
+// sequence from the slice table the split kernel recorded (one sequence per
+// lane of each wave, with a scan and a ballot), so no workgroup is launched
+// only to exit; a grid sized for the worst case had spent most of the batch
+// combine dispatching such workgroups.
+template <int kVals, bool kLoop>
+__global__ __launch_bounds__(kCombineThreads) void combine_kernel(Args a, int single_c, int max_slices,
+                                                                   int row_groups)
+{
+    constexpr int kUnits = kColBlocks * 4 / kVals;  // units per 16-row block
+    __shared__ CombineSmem<kVals> sm;
+    if constexpr (!kLoop) {
+        const int b = blockIdx.z;
+        // This sequence's slices: nvalid of them, from batch slice start on.
+        // One sequence has the host's slicing; in a batch, the split kernel
+        // recorded each sequence's range in the workspace.
+        int64_t start = 0;
+        int nvalid;
+        if (a.batch == 1) {
+            const int t1 = (seq_keys(a, 0) + kTileKeys - 1) / kTileKeys;
+            nvalid = (t1 + single_c - 1) / single_c;
+        } else {
+            start = a.seq_slices[2 * b];
+            nvalid = a.seq_slices[2 * b + 1];
+        }
+        nvalid = __builtin_amdgcn_readfirstlane(nvalid);
+        const int wpc = combine_wpc<kVals>(nvalid);
+        if ((int)blockIdx.x >= kUnits * wpc / kCombineWaves)
+            return;  // the whole workgroup (uniform)
+        combine_unit<kVals>(a, sm, b, blockIdx.y, blockIdx.x, start, nvalid, wpc, max_slices);
+    } else {
+        const int lane = threadIdx.x & 63;
+        const int rbs = row_groups * 4;  // 16-row blocks per sequence
+        int st = 0, nv = 0, items = 0, wpc_l = 1;
+        if (lane < a.batch) {
+            st = a.seq_slices[2 * lane];
+            nv = a.seq_slices[2 * lane + 1];
+            wpc_l = combine_wpc<kVals>(nv);
+            items = rbs * (kUnits * wpc_l / kCombineWaves);
+        }
+        const int incl = wave_incl_scan(items);
+        const int total = __shfl(incl, 63);
+        for (int item = blockIdx.x; item < total; item += gridDim.x) {
+            const uint64_t hit = __builtin_amdgcn_ballot_w64(items > 0 && item >= incl - items && item < incl);
+            const int b = __builtin_ctzll(hit);  // exactly one lane: the ranges are disjoint
+            const int local = item - (__shfl(incl, b) - __shfl(items, b));
+            const int wpc = __builtin_amdgcn_readfirstlane(__shfl(wpc_l, b));
+            const int per = kUnits * wpc / kCombineWaves;  // workgroup items per 16-row block
+            combine_unit<kVals>(a, sm, b, local / per, local % per, __shfl(st, b),
+                                __builtin_amdgcn_readfirstlane(__shfl(nv, b)), wpc, max_slices);
+            __syncthreads();  // the next item reuses the LDS
+        }
+    }
 }
 
 }  // namespace
@@ -888,6 +940,12 @@ hipError_t launch_combine(const Plan& p, const Args& a, hipStream_t stream)
 {
     // One sequence with many slices: half column blocks (twice the waves, 32
     // slices in flight each); otherwise whole column blocks (16 in flight).
+    if (a.batch > 1 && a.batch <= 64) {
+        // two resident workgroups per compute unit walk the batch's items
+        hipLaunchKernelGGL((combine_kernel<4, true>), dim3(2 * p.cus), dim3(kCombineThreads), 0, stream, a,
+                           p.single_c, p.max_slices, p.row_groups);
+        return hipGetLastError();
+    }
     // The grid is sized for the most waves per unit a sequence can need (it
     // has at most `slots` slices); each workgroup picks its sequence's count.
     const bool half = a.batch == 1 && p.splits > 32;
@@ -896,7 +954,7 @@ hipError_t launch_combine(const Plan& p, const Args& a, hipStream_t stream)
     int wpc = 1;
     while (wpc < kCombineWaves && wpc * unroll < p.slots)
         wpc *= 2;
-    hipLaunchKernelGGL(half ? combine_kernel<2> : combine_kernel<4>,
+    hipLaunchKernelGGL((half ? combine_kernel<2, false> : combine_kernel<4, false>),
                        dim3(units * wpc / kCombineWaves, p.row_groups * 4, a.batch), dim3(kCombineThreads), 0,
                        stream, a, p.single_c, p.max_slices, p.row_groups);
     return hipGetLastError();
