@@ -219,6 +219,21 @@ def test_many_sequences(oracle_mod, batch):
     compare(wl, oracle_mod, label=f"{batch} sequences")
 
 
+def test_batch_sequence_with_many_slices(oracle_mod):
+    """A batch whose long sequence has more slices than one round of the batch
+    combine's waves holds (8 waves x 16 slices in flight): its merge runs two
+    rounds per wave."""
+    pre = [150000, 500]
+    wl = I.make_workload(batch=2, num_nodes=8, num_heads=8, prefix_lens=pre, num_slots=262144,
+                         tree="chain", config_id=111, device="cuda", q_gain=4.0)
+    # the device's slicing: c tiles per slice, c = ceil(T / (G - (B - 1))) for G slots
+    G = torch.cuda.get_device_properties(0).multi_processor_count
+    tiles = [(p + 8 + 31) // 32 for p in pre]
+    c = -(-sum(tiles) // (G - 1))
+    assert -(-tiles[0] // c) > 8 * 16
+    compare(wl, oracle_mod, rows=sample_rows(wl, 32, seed=11), label="batch, 247-slice sequence")
+
+
 def test_batch_slicing_is_independent_of_layout_and_padding():
     """The slicing depends only on seq_lens: the same batch with a larger
     max_kv (more table columns, junk past every sequence) gives the same bits."""
