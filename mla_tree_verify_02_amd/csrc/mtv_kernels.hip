@@ -1,8 +1,9 @@
 // gfx950 kernels for absorbed-MLA tree-verify attention over a page_size=1 pool.
 //
 // split_kernel: one workgroup = one key slice of one sequence x up to 64 query
-//   rows (4 waves x 16 rows). Per slice it stages the page indices in LDS, then
-//   streams 32-key tiles through a 3-buffer LDS ring filled by direct
+//   rows (4 waves x 16 rows). Per slice it stages the page indices in LDS (by
+//   direct global->LDS word loads), then streams 32-key tiles through a
+//   3-buffer LDS ring filled by direct
 //   global->LDS 16-byte loads (each 1152-byte latent row is nine full 128-byte
 //   lines), computes S^T = K.Q^T and O^T += V^T.P^T on 16x16x32 bf16 MFMA, and
 //   keeps an online softmax (running max in log2 units, running sum) in fp32.
@@ -14,8 +15,11 @@
 //   only in tiles that reach the tree block or the end of the sequence.
 //   Slices have one length for the whole batch, derived on the device from
 //   seq_lens (slicing()), so a long sequence gets many and a short one few.
+//   Partial results go out with device-scope stores (through the XCD's L2).
 // combine_kernel: merges the slices of each row by log-sum-exp and writes the
-//   bf16 output and the natural-log lse.
+//   bf16 output and the natural-log lse; one workgroup per work item, or, for
+//   batches of 2..64 sequences, a fixed grid that walks the items the batch
+//   needs.
 #include <hip/hip_runtime.h>
 
 #include <math.h>
