@@ -77,11 +77,16 @@ static_assert(kMoveRows * kRowChunks % kMoveThreads == 0, "whole chunks per lane
 
 // Whole-sequence move, copy phase: rows of positions [0, S_b) of each sequence
 // go from their table slots to base_b + p. A workgroup copies 32 rows per pass
-// (2304 chunks, 9 per lane, all loads issued before any store), striding over
-// the batch's rows. Destination runs must not overlap any source row (the host
-// documents this), so passes need no ordering among themselves. Rows are read
-// and written once: non-temporal loads and stores keep them out of the caches.
-// Reads are clamped to the pool; destinations outside it are skipped.
+// (2304 chunks, 9 per lane), striding over the batch's rows. The passes of a
+// workgroup are software-pipelined: the table words of pass q+1 are loaded
+// before the rows of pass q are stored, and its rows are loaded right after
+// those stores are issued, so a pass's load latency overlaps the previous
+// pass's stores (vmcnt retires in order: waiting for a load never waits for
+// stores issued after it). Destination runs must not overlap any source row
+// (the host documents this), so passes need no ordering among themselves.
+// Rows are read and written once: non-temporal loads and stores keep them out
+// of the caches. Reads are clamped to the pool; destinations outside it are
+// skipped.
 __global__ __launch_bounds__(kMoveThreads) void kv_move_kernel(
     int batch, int max_kv, int64_t num_slots, u32x4* __restrict__ kv,
     const int32_t* __restrict__ table, const int32_t* __restrict__ seq_lens,
@@ -92,46 +97,89 @@ __global__ __launch_bounds__(kMoveThreads) void kv_move_kernel(
     // pass q covers rows 32q .. 32q+31 of the flattened (sequence, position)
     // space [0, batch * rows_per_seq_stride)
     const int64_t passes = ((int64_t)batch * rows_per_seq_stride + kMoveRows - 1) / kMoveRows;
-    for (int64_t q = blockIdx.x; q < passes; q += gridDim.x) {
-        // (sequence, position) of the pass's first row; one division per pass
-        const int64_t f0 = q * kMoveRows;
-        const int64_t b0 = f0 / rows_per_seq_stride;
+    int64_t q = blockIdx.x;
+    if (q >= passes)
+        return;
+
+    // Table words of pass qq for this lane's chunks: src = the source slot
+    // (clamped to the pool) or -1 (no row: past the batch or the sequence),
+    // dst = the destination slot or -1 (no row, or outside the pool). The
+    // table word, the length and the base are loaded independently; the
+    // length only decides afterwards whether the row exists.
+    auto fetch = [&](int64_t qq, int32_t* src, int32_t* dst) {
+        const int64_t f0 = qq * kMoveRows;
+        const int64_t b0 = f0 / rows_per_seq_stride;  // one division per pass
         const int64_t p0 = f0 - b0 * rows_per_seq_stride;
-        u32x4 v[kMoveLoads];
-        int32_t drow[kMoveLoads];  // destination slot, or -1
+        int32_t tv[kMoveLoads], sl[kMoveLoads], bs[kMoveLoads], pos[kMoveLoads];
 #pragma unroll
         for (int j = 0; j < kMoveLoads; ++j) {
-            const int c = j * kMoveThreads + tid;        // chunk within the pass
-            const int r = c / kRowChunks;                 // row within the pass
+            const int r = (j * kMoveThreads + tid) / kRowChunks;  // row within the pass
             int64_t pp = p0 + r;
             int64_t bb = b0;
             while (pp >= rows_per_seq_stride) {  // at most 32 / stride steps
                 pp -= rows_per_seq_stride;
                 ++bb;
             }
-            const int b = (int)(bb < batch ? bb : batch);
-            const int p = (int)pp;
-            drow[j] = -1;
-            v[j] = u32x4{0u, 0u, 0u, 0u};
-            if (b < batch) {
-                const int S = min(max(seq_lens[b], 0), max_kv);
-                if (p < S) {
-                    int64_t s = table[(int64_t)b * max_kv + p];
-                    s = s < 0 ? 0 : (s > maxslot ? maxslot : s);
-                    v[j] = __builtin_nontemporal_load(&kv[s * kRowChunks + (c - r * kRowChunks)]);
-                    const int64_t d = (int64_t)base[b] + p;
-                    if (d >= 0 && d <= maxslot)
-                        drow[j] = (int32_t)d;
-                }
+            pos[j] = -1;
+            tv[j] = 0, sl[j] = 0, bs[j] = 0;
+            if (bb < batch) {
+                pos[j] = (int)pp;  // < max_kv: inside the table row
+                tv[j] = table[bb * max_kv + pp];
+                sl[j] = seq_lens[bb];
+                bs[j] = base[bb];
             }
         }
 #pragma unroll
         for (int j = 0; j < kMoveLoads; ++j) {
+            const int S = min(max(sl[j], 0), max_kv);
+            src[j] = -1;
+            dst[j] = -1;
+            if (pos[j] >= 0 && pos[j] < S) {
+                const int64_t sv = tv[j];
+                src[j] = (int32_t)(sv < 0 ? 0 : (sv > maxslot ? maxslot : sv));
+                const int64_t d = (int64_t)bs[j] + pos[j];
+                if (d >= 0 && d <= maxslot)
+                    dst[j] = (int32_t)d;
+            }
+        }
+    };
+    auto load_rows = [&](const int32_t* src, u32x4* v) {
+#pragma unroll
+        for (int j = 0; j < kMoveLoads; ++j) {
             const int c = j * kMoveThreads + tid;
             const int r = c / kRowChunks;
-            if (drow[j] >= 0)
-                __builtin_nontemporal_store(v[j], &kv[(int64_t)drow[j] * kRowChunks + (c - r * kRowChunks)]);
+            v[j] = src[j] >= 0 ? __builtin_nontemporal_load(&kv[(int64_t)src[j] * kRowChunks + (c - r * kRowChunks)])
+                               : u32x4{0u, 0u, 0u, 0u};
         }
+    };
+    auto store_rows = [&](const int32_t* dst, const u32x4* v) {
+#pragma unroll
+        for (int j = 0; j < kMoveLoads; ++j) {
+            const int c = j * kMoveThreads + tid;
+            const int r = c / kRowChunks;
+            if (dst[j] >= 0)
+                __builtin_nontemporal_store(v[j], &kv[(int64_t)dst[j] * kRowChunks + (c - r * kRowChunks)]);
+        }
+    };
+
+    int32_t src[kMoveLoads], dst[kMoveLoads];
+    u32x4 v[kMoveLoads];
+    fetch(q, src, dst);
+    load_rows(src, v);
+    for (;;) {
+        const int64_t qn = q + gridDim.x;
+        const bool more = qn < passes;  // uniform
+        int32_t srcn[kMoveLoads], dstn[kMoveLoads];
+        if (more)
+            fetch(qn, srcn, dstn);
+        store_rows(dst, v);
+        if (!more)
+            break;
+        load_rows(srcn, v);
+#pragma unroll
+        for (int j = 0; j < kMoveLoads; ++j)
+            dst[j] = dstn[j];
+        q = qn;
     }
 }
 
@@ -165,7 +213,9 @@ hipError_t launch_kv_move(const KvArgs& a, int cus, hipStream_t stream)
     // rows per sequence slot in the flattened space: the longest possible S
     const int64_t stride = a.max_kv;
     const int64_t passes = ((int64_t)a.batch * stride + kMoveRows - 1) / kMoveRows;
-    const int64_t grid = passes < (int64_t)cus * 8 ? passes : (int64_t)cus * 8;
+    // A resident grid: the copy kernel's registers allow three workgroups per
+    // compute unit, and each workgroup loops over passes (pipelined).
+    const int64_t grid = passes < (int64_t)cus * 3 ? passes : (int64_t)cus * 3;
     hipLaunchKernelGGL(kv_move_kernel, dim3((unsigned)grid), dim3(kMoveThreads), 0, stream, a.batch,
                        a.max_kv, a.num_slots, (u32x4*)a.kv, a.page_table, a.seq_lens, a.base, stride);
     if (hipGetLastError() != hipSuccess)

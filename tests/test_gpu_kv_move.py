@@ -92,6 +92,31 @@ def test_defrag_bit_exact():
     assert np.array_equal(bits(gp), ep)
 
 
+def test_defrag_short_rows_and_runs_past_the_pool():
+    """Tables shorter than one 32-row pass (a pass spans several sequences),
+    many passes per workgroup, out-of-range table entries (clamped reads) and
+    runs that end past the pool (those rows are skipped and their table
+    entries kept)."""
+    rng = np.random.default_rng(5)
+    B, P, max_kv = 3000, 40000, 7
+    pool = rand_pool(P, 12)
+    seq = [int(x) for x in rng.integers(0, max_kv + 1, size=B)]
+    table = rng.integers(0, P // 2, size=(B, max_kv)).astype(np.int32)
+    table[rng.random((B, max_kv)) < 0.01] = -5          # clamped to slot 0
+    table[rng.random((B, max_kv)) < 0.01] = P + 123     # clamped to the last slot
+    # disjoint runs of 8 slots in the upper half, so no run holds a source: the
+    # clamped slot P - 1 would be position 7 of a run (never a row), and the
+    # last runs end past the pool
+    base = [P // 2 + 8 * b for b in range(B)]
+    assert base[-1] + max_kv > P and (P - 1 - P // 2) % 8 >= max_kv
+    gp, gt = pool.cuda(), torch.from_numpy(table).cuda()
+    M.kv_defrag(gp, gt, torch.tensor(seq, dtype=torch.int32).cuda(), torch.tensor(base, dtype=torch.int32).cuda())
+    torch.cuda.synchronize()
+    ep, et = K.kv_defrag(bits(pool), table, seq, base)
+    assert np.array_equal(gt.cpu().numpy(), et)
+    assert np.array_equal(bits(gp), ep)
+
+
 def test_defrag_at_189k_keeps_rows_and_attention():
     wl = I.config_workload(3, device="cuda", ctx=189440)
     before = [t.clone() for t in M.verify_workload(wl)]
