@@ -87,9 +87,14 @@ static_assert(kMoveRows * kRowChunks % kMoveThreads == 0, "whole chunks per lane
 // Rows are read and written once: non-temporal loads and stores keep them out
 // of the caches. Reads are clamped to the pool; destinations outside it are
 // skipped.
+// The table phase follows in the same kernel: every table word belongs to one
+// pass and every pass to one workgroup, so once all of a workgroup's waves are
+// past its last pass (one barrier), it sets table[b][p] = base_b + p for the
+// rows of its own passes whose destination lies in the pool. No other
+// workgroup reads those words.
 __global__ __launch_bounds__(kMoveThreads) void kv_move_kernel(
     int batch, int max_kv, int64_t num_slots, u32x4* __restrict__ kv,
-    const int32_t* __restrict__ table, const int32_t* __restrict__ seq_lens,
+    int32_t* __restrict__ table, const int32_t* __restrict__ seq_lens,
     const int32_t* __restrict__ base, int64_t rows_per_seq_stride)
 {
     const int tid = threadIdx.x;
@@ -181,20 +186,20 @@ __global__ __launch_bounds__(kMoveThreads) void kv_move_kernel(
             dst[j] = dstn[j];
         q = qn;
     }
-}
 
-// Whole-sequence move, table phase (after the copy phase on the same stream):
-// table[b][p] = base_b + p for p < S_b whose destination lies in the pool.
-__global__ __launch_bounds__(kMoveThreads) void kv_move_table_kernel(
-    int batch, int max_kv, int64_t num_slots, int32_t* __restrict__ table,
-    const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ base)
-{
-    const int b = blockIdx.y;
-    const int S = min(max(seq_lens[b], 0), max_kv);
-    for (int p = blockIdx.x * kMoveThreads + threadIdx.x; p < S; p += gridDim.x * kMoveThreads) {
-        const int64_t d = (int64_t)base[b] + p;
-        if (d >= 0 && d < num_slots)
-            table[(int64_t)b * max_kv + p] = (int32_t)d;
+    // Table phase for this workgroup's passes: one thread per row.
+    __syncthreads();  // every wave has read its table words
+    if (tid < kMoveRows) {
+        for (int64_t qq = blockIdx.x; qq < passes; qq += gridDim.x) {
+            const int64_t f = qq * kMoveRows + tid;
+            const int64_t bb = f / rows_per_seq_stride;
+            const int64_t pp = f - bb * rows_per_seq_stride;
+            if (bb < batch && pp < min(max(seq_lens[bb], 0), max_kv)) {
+                const int64_t d = (int64_t)base[bb] + pp;
+                if (d >= 0 && d <= maxslot)
+                    table[bb * max_kv + pp] = (int32_t)d;
+            }
+        }
     }
 }
 
@@ -218,11 +223,6 @@ hipError_t launch_kv_move(const KvArgs& a, int cus, hipStream_t stream)
     const int64_t grid = passes < (int64_t)cus * 3 ? passes : (int64_t)cus * 3;
     hipLaunchKernelGGL(kv_move_kernel, dim3((unsigned)grid), dim3(kMoveThreads), 0, stream, a.batch,
                        a.max_kv, a.num_slots, (u32x4*)a.kv, a.page_table, a.seq_lens, a.base, stride);
-    if (hipGetLastError() != hipSuccess)
-        return hipErrorLaunchFailure;
-    const int xb = (a.max_kv + kMoveThreads - 1) / kMoveThreads;
-    hipLaunchKernelGGL(kv_move_table_kernel, dim3(xb < 1024 ? xb : 1024, a.batch), dim3(kMoveThreads), 0,
-                       stream, a.batch, a.max_kv, a.num_slots, a.page_table, a.seq_lens, a.base);
     return hipGetLastError();
 }
 
