@@ -133,6 +133,30 @@ def time_each_call(calls, steps, torch, fn="run"):
     return sorted(a.elapsed_time(b) * 1e3 for a, b in ev)
 
 
+SPIN_CYCLES = 200_000  # torch.cuda._sleep cycles queued ahead of each timed small call
+
+
+def time_each_call_gpu(fn, steps, torch, before=None):
+    """Per-call GPU durations (us) of small calls: HIP events around each call
+    on torch's current stream, with a short spin kernel queued ahead of the
+    events so that the GPU is still busy while the host enqueues the events
+    and the call (host time then stays outside the bracket). `before(k)`
+    enqueues untimed work ahead of the spin. Returns the sorted list."""
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    torch.cuda.synchronize()
+    for k in range(steps):
+        if before is not None:
+            before(k)
+        torch.cuda._sleep(SPIN_CYCLES)
+        ev[k][0].record(stream)
+        fn(k)
+        ev[k][1].record(stream)
+    torch.cuda.synchronize()
+    return sorted(a.elapsed_time(b) * 1e3 for a, b in ev)
+
+
 def pct(sorted_us, q):
     return sorted_us[min(len(sorted_us) - 1, int(q * len(sorted_us)))]
 
@@ -279,11 +303,15 @@ def other_configs(args, torch, M, I):
                 def run(self):
                     M.tree_mask_build(parents, out=mask)
             us = time_each_call([_Call()], 200, torch)
+            gus = time_each_call_gpu(lambda k: M.tree_mask_build(parents, out=mask), 200, torch)
             res["b%d_n%d" % (b, n)] = {"us_per_call": {"p10": round(pct(us, 0.1), 2),
                                                        "p50": round(pct(us, 0.5), 2),
                                                        "p90": round(pct(us, 0.9), 2)},
-                                       "nodes_per_s": round(b * n / (pct(us, 0.5) * 1e-6), 1)}
-            log("tree mask build B=%d N=%d: %.2f us/call" % (b, n, pct(us, 0.5)))
+                                       "gpu_us": {"p10": round(pct(gus, 0.1), 2), "p50": round(pct(gus, 0.5), 2),
+                                                  "p90": round(pct(gus, 0.9), 2)},
+                                       "nodes_per_s": round(b * n / (pct(gus, 0.5) * 1e-6), 1)}
+            log("tree mask build B=%d N=%d: %.2f us/call (%.2f us on the GPU)"
+                % (b, n, pct(us, 0.5), pct(gus, 0.5)))
         out["tree_mask_build"] = res
     if "kv" in names:
         out["kv_moves"] = kv_moves(torch, M, I)
@@ -360,11 +388,16 @@ def kv_moves(torch, M, I):
                 ev.append((e0, e1))
         torch.cuda.synchronize()
         us = sorted(a.elapsed_time(b) * 1e3 for a, b in ev)
+        gus = time_each_call_gpu(lambda k: M.kv_commit(pool, work, seq, N, alen, apath, base), 200, torch,
+                                 before=lambda k: work.copy_(table0))
         res["commit_b%d_n%d_l%d" % (B, N, len(path))] = {
             "us_per_call": {"p10": round(pct(us, 0.1), 2), "p50": round(pct(us, 0.5), 2),
                             "p90": round(pct(us, 0.9), 2)},
+            "gpu_us": {"p10": round(pct(gus, 0.1), 2), "p50": round(pct(gus, 0.5), 2),
+                       "p90": round(pct(gus, 0.9), 2)},
             "rows_moved": B * len(path)}
-        log("commit B=%d N=%d L=%d: %.2f us/call" % (B, N, len(path), pct(us, 0.5)))
+        log("commit B=%d N=%d L=%d: %.2f us/call (%.2f us on the GPU)"
+            % (B, N, len(path), pct(us, 0.5), pct(gus, 0.5)))
         del pool
     return res
 
