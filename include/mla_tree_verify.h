@@ -284,8 +284,9 @@ int mla_kv_commit(int32_t batch,
  * destination runs must not overlap any source row or each other (for
  * instance, a freshly allocated region); otherwise the result is unspecified
  * (never out of bounds: reads are clamped to the pool, destinations outside it
- * skipped). Pointers as for mla_kv_commit. Two launches: the copy, then the
- * table rewrite.
+ * skipped). Pointers as for mla_kv_commit. One launch: the copy, with each
+ * workgroup rewriting the table entries of the rows it moved once all of them
+ * have been read.
  * Returns MTV_OK or MTV_ERR_NULL / MTV_ERR_SHAPE / MTV_ERR_ALIGN / MTV_ERR_HIP.
  */
 int mla_kv_defrag(int32_t batch,
