@@ -314,8 +314,22 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(Args a, int slots, i
     int b = 0;
     int split = gslice;
     int S = sk;
-    if (a.batch == 1 && gslice >= nslices)
-        return;  // the whole workgroup: a sequence shorter than max_kv
+    if (a.batch == 1 && gslice >= nslices) {
+        // A sequence shorter than max_kv: this slice holds none of its keys.
+        // Its slots get the empty partial, (max, sum) = (-inf, 0) and O = 0,
+        // so that the combine can merge every slice the host planned for
+        // max_kv without waiting for seq_lens (stale slots would hold another
+        // call's values).
+        const size_t pz = (size_t)grp * max_slices + gslice;
+        if (tid < kRowsPerGroup) {
+            float2* pm = (float2*)a.part_ml + pz * kRowsPerGroup + tid;
+            *pm = make_float2(-INFINITY, 0.f);
+        }
+        uint4* po = (uint4*)((__bf16*)a.part_o + pz * (size_t)(kRowsPerGroup * kPartRowElems));
+        for (int i = tid; i < kRowsPerGroup * kPartRowElems * 2 / 16; i += kThreads)
+            po[i] = uint4{0u, 0u, 0u, 0u};
+        return;  // the whole workgroup
+    }
     if (__builtin_expect(a.batch > 1 && a.batch <= kWaveBatch, 0)) {
         // one sequence per lane: the lane whose slice range holds gslice
         const int nl = (int)((tb + c - 1) / c);
@@ -762,7 +776,7 @@ struct CombineSmem {
     fvec o[kCombineWaves][64];
 };
 
-template <int kVals>
+template <int kVals, bool kZeroEmpty>
 __device__ __forceinline__ void combine_unit(const Args& a, CombineSmem<kVals>& sm, int b, int rb, int xblk,
                                              int64_t start, int nvalid, int wpc, int max_slices)
 {
@@ -808,6 +822,12 @@ __device__ __forceinline__ void combine_unit(const Args& a, CombineSmem<kVals>& 
         for (int u = 0; u < kUnroll; ++u) {
             if (s0 + u * wpc >= nvalid)
                 ml[u] = make_float2(-INFINITY, 0.f);  // past the sequence: weight 0
+            // A slice with no visible key has O = 0 already. Selecting it
+            // explicitly changes how the compiler orders the loads, which is
+            // measured faster in the batch combine (11.3 -> 9.7 us, batch 8)
+            // and not in the one-sequence grid.
+            if (kZeroEmpty && ml[u].x == -INFINITY)
+                ov[u] = bvec{};
             mx = fmaxf(mx, ml[u].x);
         }
         if (mx == -INFINITY)
@@ -887,13 +907,15 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(Args a, int si
     if constexpr (!kLoop) {
         const int b = blockIdx.z;
         // This sequence's slices: nvalid of them, from batch slice start on.
-        // One sequence has the host's slicing; in a batch, the split kernel
-        // recorded each sequence's range in the workspace.
+        // One sequence has the host's slicing (for max_kv, known before any
+        // load); in a batch, the split kernel recorded each sequence's range
+        // in the workspace.
         int64_t start = 0;
         int nvalid;
         if (a.batch == 1) {
-            const int t1 = (seq_keys(a, 0) + kTileKeys - 1) / kTileKeys;
-            nvalid = (t1 + single_c - 1) / single_c;
+            // every slice the host planned for max_kv: those past a shorter
+            // sequence hold (-inf, 0), written by the split kernel
+            nvalid = max_slices;
         } else {
             start = a.seq_slices[2 * b];
             nvalid = a.seq_slices[2 * b + 1];
@@ -902,7 +924,7 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(Args a, int si
         const int wpc = combine_wpc<kVals>(nvalid);
         if ((int)blockIdx.x >= kUnits * wpc / kCombineWaves)
             return;  // the whole workgroup (uniform)
-        combine_unit<kVals>(a, sm, b, blockIdx.y, blockIdx.x, start, nvalid, wpc, max_slices);
+        combine_unit<kVals, false>(a, sm, b, blockIdx.y, blockIdx.x, start, nvalid, wpc, max_slices);
     } else {
         const int lane = threadIdx.x & 63;
         const int rbs = row_groups * 4;  // 16-row blocks per sequence
@@ -921,7 +943,7 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(Args a, int si
             const int local = item - (__shfl(incl, b) - __shfl(items, b));
             const int wpc = __builtin_amdgcn_readfirstlane(__shfl(wpc_l, b));
             const int per = kUnits * wpc / kCombineWaves;  // workgroup items per 16-row block
-            combine_unit<kVals>(a, sm, b, local / per, local % per, __shfl(st, b),
+            combine_unit<kVals, true>(a, sm, b, local / per, local % per, __shfl(st, b),
                                 __builtin_amdgcn_readfirstlane(__shfl(nv, b)), wpc, max_slices);
             __syncthreads();  // the next item reuses the LDS
         }

@@ -42,9 +42,10 @@ def run_gpu(wl):
             lse.cpu().numpy())
 
 
-def compare(wl, oracle_mod, rows=None, label=""):
-    """Run both sides; compare all rows or the given flat row ids."""
-    g_out, g_lse = run_gpu(wl)
+def compare(wl, oracle_mod, rows=None, label="", gpu=None):
+    """Run both sides (or take the GPU's (out bits, lse) from `gpu`); compare
+    all rows or the given flat row ids."""
+    g_out, g_lse = run_gpu(wl) if gpu is None else gpu
     o_out, o_lse = oracle_mod.run_workload(wl, rows=rows)
     g_out = bf16_bits_to_f32(g_out).reshape(-1, 512)
     o_out = bf16_bits_to_f32(o_out).reshape(-1, 512)
@@ -232,6 +233,22 @@ def test_batch_sequence_with_many_slices(oracle_mod):
     c = -(-sum(tiles) // (G - 1))
     assert -(-tiles[0] // c) > 8 * 16
     compare(wl, oracle_mod, rows=sample_rows(wl, 32, seed=11), label="batch, 247-slice sequence")
+
+
+def test_one_sequence_shorter_than_max_kv_ignores_stale_workspace(oracle_mod):
+    """One sequence with far fewer keys than max_kv: the plan has slices for
+    max_kv, the combine loads all of them, and the ones this call did not
+    write (here a workspace of NaN bytes) must get no weight."""
+    wl = I.make_workload(batch=1, num_nodes=16, num_heads=8, prefix_lens=[3000], num_slots=65536,
+                         tree="binary", config_id=112, device="cuda", max_kv=40000, q_gain=4.0)
+    shape = M.make_shape(1, 16, 8, wl.max_kv, wl.num_slots)
+    plan = M.plan_query(shape, torch.cuda.get_device_properties(0).multi_processor_count)
+    assert plan["splits"] * plan["chunk"] >= 40000 and plan["chunk"] < 3016 // 4
+    ws = torch.full((M.workspace_size(shape),), 0xFF, dtype=torch.uint8, device="cuda")
+    out, lse = M.verify_workload(wl, workspace=ws)
+    torch.cuda.synchronize()
+    compare(wl, oracle_mod, label="short sequence, NaN workspace",
+            gpu=(out.view(torch.int16).cpu().numpy().view(np.uint16), lse.cpu().numpy()))
 
 
 def test_batch_slicing_is_independent_of_layout_and_padding():
