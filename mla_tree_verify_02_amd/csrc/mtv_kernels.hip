@@ -532,9 +532,14 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(Args a, int slots, i
         issue(1, idx_n);
     }
 
-    constexpr int kKGroup = 6;            // K-operand reads per group (double-buffered)
+    // K-operand reads per group (double-buffered): groups of 4 give 9 groups,
+    // one per row gather of tile t+2 (measured against groups of 6 with the
+    // last three gathers in the P.V: 2 % faster on 128 rows, 3-5 % on the
+    // MFMA-bound 64 x 64 heads, same elsewhere, bit-identical)
+    constexpr int kKGroup = 4;
     constexpr int kKReads = 2 * kKSteps;  // 36 per tile (two key blocks)
     constexpr int kVGroup = 4;            // column blocks per V-operand group
+    constexpr int kKGroups = kKReads / kKGroup;
 
     // Tile t's rows are in LDS once at most the rows of tile t+1 remain
     // outstanding and every wave has passed the barrier; the barrier also
@@ -566,11 +571,13 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(Args a, int slots, i
             const char LDS_AS* kb1 = buf + koff1;
             const int base = k0 + t * kTileKeys;
             // Tile t+2's rows go into the buffer tile t-1 used, spread over
-            // this tile's Q.K^T so that the address unit works while the MFMAs
-            // issue. Past the last tile (and when a raised reference makes
-            // this tile run again) the same loads go out again from the last
-            // staged indices into that free buffer: identical or never-read
-            // bytes, rows already in L2, and waits that only get stricter.
+            // this tile's Q.K^T (one per K-operand group; any left over go
+            // between V^T groups of the P.V) so that the address unit works
+            // while the MFMAs issue. Past the last tile (and when a raised
+            // reference makes this tile run again) the same loads go out again
+            // from the last staged indices into that free buffer: identical or
+            // never-read bytes, rows already in L2, and waits that only get
+            // stricter.
             const uint32_t gdst = lds0 + (uint32_t)(((t + 2) % kStages) * kTileBytes +
                                                     wave * (kKeysPerWave * kRowBytes));
 
@@ -594,8 +601,8 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(Args a, int slots, i
                         kf[(g + 1) & 1][j] =
                             *(const bf16x8 LDS_AS*)kptr((g + 1) * kKGroup + j);
                 }
-                // gathers of tile t+2: load g here, loads 6-8 in the P.V below
-                gather16_to_lds(kv + (int64_t)idx_n[g] * kRowBytes + gco[g], gdst + g * 1024);
+                if (g < kLoadsPerWave)
+                    gather16_to_lds(kv + (int64_t)idx_n[g] * kRowBytes + gco[g], gdst + g * 1024);
 #pragma unroll
                 for (int j = 0; j < kKGroup; ++j) {
                     const int n = g * kKGroup + j;
@@ -618,15 +625,15 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(Args a, int slots, i
             for (int k = 0; k < 8; ++k)
                 x[k] = sacc[k >> 2][k & 3] * scale_log2;
 
-            // keep six K-operand reads in flight ahead of the Q.K^T MFMAs
-            __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+            // keep one group of K-operand reads in flight ahead of the Q.K^T MFMAs
+            __builtin_amdgcn_sched_group_barrier(0x100, kKGroup, 0);
 #pragma unroll
-            for (int i = 0; i < 30; ++i) {
+            for (int i = 0; i < kKReads - kKGroup; ++i) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
                 __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
             }
-            __builtin_amdgcn_sched_group_barrier(0x008, 6, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, kKGroup, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2 * kVGroup, 0);
             if (base + kTileKeys > tree0) {
                 // tail tile: tree bitmask and the end of the sequence
 #pragma unroll
@@ -680,9 +687,14 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(Args a, int slots, i
                             (bf16x4 LDS_AS*)(vptr(cb) + 16 * kRowBytes));
                     }
                 }
-                if ((g & 1) && g < 7) {
-                    const int j = 6 + (g >> 1);
-                    gather16_to_lds(kv + (int64_t)idx_n[j] * kRowBytes + gco[j], gdst + j * 1024);
+                {
+                    // the gathers the Q.K^T groups did not issue, spread evenly
+                    // over the P.V groups
+                    constexpr int kRest = kLoadsPerWave > kKGroups ? kLoadsPerWave - kKGroups : 0;
+                    constexpr int kVGs = kColBlocks / kVGroup;
+#pragma unroll
+                    for (int j = kKGroups + g * kRest / kVGs; j < kKGroups + (g + 1) * kRest / kVGs; ++j)
+                        gather16_to_lds(kv + (int64_t)idx_n[j] * kRowBytes + gco[j], gdst + j * 1024);
                 }
 #pragma unroll
                 for (int c = 0; c < kVGroup; ++c) {
@@ -695,11 +707,11 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(Args a, int slots, i
 
             // two transposed V reads per P.V MFMA, eight ahead
 #pragma unroll
-            for (int i = 0; i < 28; ++i) {
+            for (int i = 0; i < kColBlocks - kVGroup; ++i) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
                 __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
             }
-            __builtin_amdgcn_sched_group_barrier(0x008, 4, 1);
+            __builtin_amdgcn_sched_group_barrier(0x008, kVGroup, 1);
             if (++t >= ntiles)
                 break;
             next_tile(t);
