@@ -155,6 +155,34 @@ def test_positions_past_seq_len_are_not_read():
     assert np.array_equal(got[0], base[0]) and np.array_equal(got[1], base[1])
 
 
+@pytest.mark.parametrize("prefix", [3, 100, 3000, 39979])
+def test_one_sequence_table_past_seq_len_is_not_read(oracle_mod, prefix):
+    """One sequence whose plan covers max_kv keys: the table past its end
+    names a NaN row (or an out-of-range slot, clamped to the pool's last
+    row). The last tile's positions past the end must reuse a valid row; any
+    use of the NaN row, even at weight zero, would make the outputs NaN. The
+    lengths put the end in the first tile, mid-slice and near max_kv."""
+    n, h, max_kv = 16, 8, 40000
+    wl = I.make_workload(batch=1, num_nodes=n, num_heads=h, prefix_lens=[prefix], num_slots=65536,
+                         tree="binary", config_id=113, device="cuda", max_kv=max_kv, q_gain=4.0)
+    S = prefix + n
+    base = run_gpu(wl)
+    live = set(wl.page_table[0, :S].tolist())
+    free = int(wl.page_table[0, S].item()) if S < max_kv else None
+    assert free is not None and free not in live
+    t = wl.page_table.clone()
+    t[0, S + 40:] = 10 ** 9
+    wl.page_table = t
+    wl.kv_pool[free] = float("nan")
+    if wl.num_slots - 1 not in live:
+        wl.kv_pool[wl.num_slots - 1] = float("nan")
+    got = run_gpu(wl)
+    assert np.array_equal(got[0], base[0])
+    assert np.array_equal(got[1].view(np.uint32), base[1].view(np.uint32))
+    compare(wl, oracle_mod, rows=sample_rows(wl, 16, seed=prefix), label=f"table past S={S}",
+            gpu=got)
+
+
 # ------------------------------------------------------------ full-size configs
 
 @pytest.mark.parametrize("q_gain", [1.0, 4.0])
