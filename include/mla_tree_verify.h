@@ -298,6 +298,37 @@ int mla_kv_defrag(int32_t batch,
                   const int32_t* region_base,
                   hipStream_t stream);
 
+/*
+ * Count, on `stream`, the device-resident inputs of mla_tree_verify that lie
+ * outside their ranges. The attention itself only clamps them (checking them
+ * on the host would cost a copy and a synchronisation per call). The inputs
+ * are the ones the operation above defines: the per-token page table ("The
+ * 130x Slowdown", The Reasoning, step 4), S_b = prefix length + N and the
+ * per-node tree bitmask ("The Moment of Certainty", The Path Forward).
+ *
+ * counts (uint64 [3], device memory, 8-byte aligned) is overwritten with:
+ *   counts[0]  sequences b with seq_lens[b] outside [N, max_kv];
+ *   counts[1]  table entries page_table[b][p] outside [0, num_slots), over
+ *              the positions p < S_b that the attention reads, S_b =
+ *              seq_lens[b] clamped to [N, max_kv];
+ *   counts[2]  mask rows (b, i) with a bit set for a node j >= N (in the last
+ *              word of the row; the attention ignores such bits).
+ * All zero means every index the attention reads is in range. The other
+ * device pointers (page_table int32 [B][max_kv], seq_lens int32 [B],
+ * tree_mask uint32 [B][N][W]) are as for mla_tree_verify, read only, 4-byte
+ * aligned. shape->num_heads is not used. Nothing is allocated or
+ * synchronised, and the counters are cleared by a kernel (no memset), so the
+ * call may be captured into a HIP graph; the caller reads counts after the
+ * stream reaches it.
+ * Returns MTV_OK or MTV_ERR_NULL / MTV_ERR_SHAPE / MTV_ERR_ALIGN / MTV_ERR_HIP.
+ */
+int mtv_check_inputs(const mtv_shape* shape,
+                     const int32_t* page_table,
+                     const int32_t* seq_lens,
+                     const uint32_t* tree_mask,
+                     uint64_t* counts,
+                     hipStream_t stream);
+
 /* Static, human-readable text for a status code. */
 const char* mtv_status_string(int status);
 

@@ -20,7 +20,8 @@ STATUS_NAMES = {0: "MTV_OK", -1: "MTV_ERR_NULL", -2: "MTV_ERR_SHAPE", -3: "MTV_E
                 -4: "MTV_ERR_WORKSPACE", -5: "MTV_ERR_HIP"}
 EXPORTED = ("mla_tree_verify", "mla_tree_verify_workspace_size", "mtv_status_string",
             "mtv_plan_query", "mla_tree_verify_splitkv", "mla_tree_verify_combine",
-            "mla_tree_mask_build", "mla_kv_commit", "mla_kv_defrag", "mla_tree_verify_paged")
+            "mla_tree_mask_build", "mla_kv_commit", "mla_kv_defrag", "mla_tree_verify_paged",
+            "mtv_check_inputs")
 
 
 class MtvShape(ctypes.Structure):
@@ -76,6 +77,8 @@ def load(path: Optional[str] = None):
     lib.mla_kv_commit.argtypes = [I32, I32, I32, I64, VP, VP, VP, VP, VP, VP, VP]
     lib.mla_kv_defrag.restype = ctypes.c_int
     lib.mla_kv_defrag.argtypes = [I32, I32, I64, VP, VP, VP, VP, VP]
+    lib.mtv_check_inputs.restype = ctypes.c_int
+    lib.mtv_check_inputs.argtypes = [SP, VP, VP, VP, VP, VP]
     if path is None:
         _lib = lib
     return lib
@@ -326,6 +329,38 @@ def kv_defrag(kv_pool: torch.Tensor, page_table: torch.Tensor, seq_lens: torch.T
                                _ptr(region_base), _stream_handle(dev, stream))
     if rc != MTV_OK:
         raise MtvError(rc, status_string(rc))
+
+
+def check_inputs(page_table: torch.Tensor, seq_lens: torch.Tensor, tree_mask: torch.Tensor,
+                 num_slots: int, counts: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Count out-of-range device inputs of mla_tree_verify on the GPU (see
+    mtv_check_inputs): returns int64 [3] on the device, (bad sequence
+    lengths, bad table entries below each clamped length, mask rows with bits
+    past the last node). Asynchronous: read it after the stream gets there."""
+    dev = page_table.device
+    if dev.type != "cuda":
+        raise ValueError("page_table must be on a GPU")
+    if page_table.dim() != 2 or tree_mask.dim() != 3:
+        raise ValueError("page_table must be [B, max_kv] and tree_mask [B, N, W]")
+    B, max_kv = page_table.shape
+    N = tree_mask.shape[1]
+    _check(page_table, "page_table", torch.int32, (B, max_kv), dev)
+    _check(seq_lens, "seq_lens", torch.int32, (B,), dev)
+    if tree_mask.dtype not in (torch.int32, getattr(torch, "uint32", torch.int32)):
+        raise TypeError("tree_mask must hold 32-bit words")
+    _check(tree_mask, "tree_mask", tree_mask.dtype, (B, N, (N + 31) // 32), dev)
+    if counts is None:
+        counts = torch.empty(3, dtype=torch.int64, device=dev)
+    else:
+        _check(counts, "counts", torch.int64, (3,), dev)
+    shape = make_shape(B, N, 1, max_kv, num_slots)
+    lib = load()
+    with torch.cuda.device(dev):
+        rc = lib.mtv_check_inputs(ctypes.byref(shape), _ptr(page_table), _ptr(seq_lens),
+                                  _ptr(tree_mask), _ptr(counts), _stream_handle(dev, stream))
+    if rc != MTV_OK:
+        raise MtvError(rc, status_string(rc))
+    return counts
 
 
 def verify_workload(wl, **kw):

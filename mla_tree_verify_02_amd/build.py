@@ -11,7 +11,8 @@ CSRC = os.path.join(PKG, "csrc")
 LIB_NAME = "libmla_tree_verify.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 SOURCES = [os.path.join(CSRC, "mtv_api.cpp"), os.path.join(CSRC, "mtv_kernels.hip"),
-           os.path.join(CSRC, "mtv_tree.hip"), os.path.join(CSRC, "mtv_kv.hip")]
+           os.path.join(CSRC, "mtv_tree.hip"), os.path.join(CSRC, "mtv_kv.hip"),
+           os.path.join(CSRC, "mtv_check.hip")]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

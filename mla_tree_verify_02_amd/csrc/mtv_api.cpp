@@ -305,6 +305,27 @@ int mla_kv_defrag(int32_t batch, int32_t max_kv, int64_t num_slots, void* kv_poo
     return MTV_OK;
 }
 
+int mtv_check_inputs(const mtv_shape* shape, const int32_t* page_table, const int32_t* seq_lens,
+                     const uint32_t* tree_mask, uint64_t* counts, hipStream_t stream)
+{
+    if (!shape || !page_table || !seq_lens || !tree_mask || !counts)
+        return MTV_ERR_NULL;
+    const mtv_shape& s = *shape;
+    if (s.batch < 1 || s.batch > MTV_MAX_BATCH || s.num_nodes < 1 || s.num_nodes > MTV_MAX_NODES ||
+        s.max_kv < s.num_nodes || s.max_kv > MTV_MAX_KV || s.num_slots < 1 || s.num_slots > INT32_MAX)
+        return MTV_ERR_SHAPE;
+    if (!aligned(page_table, 4) || !aligned(seq_lens, 4) || !aligned(tree_mask, 4) ||
+        !aligned(counts, 8))
+        return MTV_ERR_ALIGN;
+    const int cus = current_cu_count();
+    if (cus <= 0)
+        return MTV_ERR_HIP;
+    if (mtv::launch_check_inputs(s.batch, s.num_nodes, s.max_kv, s.num_slots, page_table, seq_lens,
+                                 tree_mask, (unsigned long long*)counts, cus, stream) != hipSuccess)
+        return MTV_ERR_HIP;
+    return MTV_OK;
+}
+
 const char* mtv_status_string(int status)
 {
     switch (status) {

@@ -67,4 +67,12 @@ hipError_t launch_tree_mask(int batch, int nodes, const int32_t* parents, uint32
 hipError_t launch_kv_commit(const KvArgs& a, hipStream_t stream);
 hipError_t launch_kv_move(const KvArgs& a, int cus, hipStream_t stream);
 
+// Counters written by the input check: out-of-range sequence lengths, table
+// entries, and mask rows with bits past the last node.
+constexpr int kCheckCounts = 3;
+hipError_t launch_check_inputs(int batch, int nodes, int max_kv, int64_t num_slots,
+                               const int32_t* page_table, const int32_t* seq_lens,
+                               const uint32_t* mask, unsigned long long* counts, int cus,
+                               hipStream_t stream);
+
 }  // namespace mtv

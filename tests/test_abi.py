@@ -168,3 +168,22 @@ def test_paged_entry_rejects_bad_arguments():
     assert call(scale=float("nan")) == -2
     assert call(pages=g + 2) == -3
     assert call(tree=g + 1) == -3
+
+
+def test_input_check_rejects_bad_arguments():
+    lib = M.load()
+    V = ctypes.c_void_p
+    g = 1 << 20
+
+    def call(shape=(1, 8, 8, 1032, 4096), pt=g, sl=g, mk=g, counts=g):
+        s = M.make_shape(*shape)
+        return lib.mtv_check_inputs(ctypes.byref(s), V(pt), V(sl), V(mk), V(counts), None)
+
+    assert lib.mtv_check_inputs(None, V(g), V(g), V(g), V(g), None) == -1
+    assert call(pt=None) == -1
+    assert call(counts=None) == -1
+    for shape in [(0, 8, 8, 1032, 4096), (1, 0, 8, 1032, 4096), (1, 65, 8, 1032, 4096),
+                  (1, 8, 8, 7, 4096), (1, 8, 8, 1032, 0), (1, 8, 8, 1032, 1 << 31)]:
+        assert call(shape=shape) == -2, shape
+    assert call(sl=g + 2) == -3
+    assert call(counts=g + 4) == -3   # the counters are 64-bit
