@@ -313,6 +313,18 @@ def other_configs(args, torch, M, I):
             log("tree mask build B=%d N=%d: %.2f us/call (%.2f us on the GPU)"
                 % (b, n, pct(us, 0.5), pct(gus, 0.5)))
         out["tree_mask_build"] = res
+        # the device input check on the headline's inputs (table, lengths, mask)
+        wl = I.config_workload(2, device="cuda")
+        counts = M.check_inputs(wl.page_table, wl.seq_lens, wl.tree_mask, wl.num_slots)
+        gus = time_each_call_gpu(lambda k: M.check_inputs(wl.page_table, wl.seq_lens, wl.tree_mask,
+                                                          wl.num_slots, counts=counts), 200, torch)
+        out["input_check"] = {"workload": "binary16-ctx65536 (65,552 table positions)",
+                              "counts": [int(x) for x in counts.cpu()],
+                              "gpu_us": {"p10": round(pct(gus, 0.1), 2), "p50": round(pct(gus, 0.5), 2),
+                                         "p90": round(pct(gus, 0.9), 2)}}
+        log("input check binary16-ctx65536: %.2f us on the GPU, counts %s"
+            % (pct(gus, 0.5), out["input_check"]["counts"]))
+        del wl
     if "kv" in names:
         out["kv_moves"] = kv_moves(torch, M, I)
     return out
