@@ -59,6 +59,13 @@ extern "C" {
                                  4-byte array or the workspace misaligned     */
 #define MTV_ERR_WORKSPACE -4  /* workspace_bytes below the required size     */
 #define MTV_ERR_HIP -5        /* the HIP runtime refused a query or a launch */
+#define MTV_ERR_SCRATCH -6    /* mla_tree_verify_noalloc: the call needs more
+                                 than MTV_NOALLOC_SCRATCH_BYTES of workspace  */
+
+/* Size of the fixed device scratch that mla_tree_verify_noalloc uses in
+ * place of a caller workspace (one copy per GPU, held until the process
+ * ends). */
+#define MTV_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
 
 /*
  * Problem shape. All fields are host values.
@@ -328,6 +335,38 @@ int mtv_check_inputs(const mtv_shape* shape,
                      const uint32_t* tree_mask,
                      uint64_t* counts,
                      hipStream_t stream);
+
+/*
+ * mla_tree_verify for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same arguments, semantics, validation and errors as mla_tree_verify, minus
+ * the workspace: the per-slice partials live in a fixed array of
+ * MTV_NOALLOC_SCRATCH_BYTES inside the library, one copy per GPU, whose device
+ * address is looked up on the first call on each device. The call never
+ * allocates, frees or synchronises.
+ *
+ * Limit: a call whose mla_tree_verify_workspace_size(shape) exceeds
+ * MTV_NOALLOC_SCRATCH_BYTES returns MTV_ERR_SCRATCH and enqueues nothing
+ * (compare the two beforehand to know). On a 256-CU MI355X one sequence of
+ * up to 16,384 query rows (N * H) fits at any context (about 17 MB), as do
+ * batches of up to 128 sequences of 8 nodes x 8 heads, or up to 64 of 16 x 8.
+ *
+ * Sharing: every call on one GPU uses that GPU's one array, which keeps the
+ * last call's contents (nothing in it needs clearing: a call writes every word
+ * it reads). Calls that may overlap on one GPU race on it -- calls on
+ * different streams, or from different threads, must be ordered by the caller
+ * (events or one stream). Calls on different GPUs do not interact.
+ */
+int mla_tree_verify_noalloc(const mtv_shape* shape,
+                            const void* q,
+                            const void* kv_pool,
+                            const int32_t* page_table,
+                            const int32_t* seq_lens,
+                            const uint32_t* tree_mask,
+                            float scale,
+                            void* out,
+                            float* lse,
+                            hipStream_t stream);
 
 /* Static, human-readable text for a status code. */
 const char* mtv_status_string(int status);

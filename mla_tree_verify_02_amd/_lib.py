@@ -17,11 +17,12 @@ from .build import LIB_PATH
 
 MTV_OK = 0
 STATUS_NAMES = {0: "MTV_OK", -1: "MTV_ERR_NULL", -2: "MTV_ERR_SHAPE", -3: "MTV_ERR_ALIGN",
-                -4: "MTV_ERR_WORKSPACE", -5: "MTV_ERR_HIP"}
+                -4: "MTV_ERR_WORKSPACE", -5: "MTV_ERR_HIP", -6: "MTV_ERR_SCRATCH"}
+NOALLOC_SCRATCH_BYTES = 32 << 20  # MTV_NOALLOC_SCRATCH_BYTES
 EXPORTED = ("mla_tree_verify", "mla_tree_verify_workspace_size", "mtv_status_string",
             "mtv_plan_query", "mla_tree_verify_splitkv", "mla_tree_verify_combine",
             "mla_tree_mask_build", "mla_kv_commit", "mla_kv_defrag", "mla_tree_verify_paged",
-            "mtv_check_inputs")
+            "mtv_check_inputs", "mla_tree_verify_noalloc")
 
 
 class MtvShape(ctypes.Structure):
@@ -55,6 +56,8 @@ def load(path: Optional[str] = None):
     lib.mla_tree_verify.restype = ctypes.c_int
     lib.mla_tree_verify.argtypes = [SP, VP, VP, VP, VP, VP, ctypes.c_float, VP, VP, VP,
                                     ctypes.c_size_t, VP]
+    lib.mla_tree_verify_noalloc.restype = ctypes.c_int
+    lib.mla_tree_verify_noalloc.argtypes = [SP, VP, VP, VP, VP, VP, ctypes.c_float, VP, VP, VP]
     lib.mla_tree_verify_splitkv.restype = ctypes.c_int
     lib.mla_tree_verify_splitkv.argtypes = [SP, VP, VP, VP, VP, VP, ctypes.c_float, VP,
                                             ctypes.c_size_t, VP]
@@ -181,6 +184,41 @@ def mla_tree_verify(q: torch.Tensor, kv_pool: torch.Tensor, page_table: torch.Te
                                  _ptr(lse), _ptr(workspace),
                                  ctypes.c_size_t(workspace.numel() * workspace.element_size()),
                                  handle)
+    if rc != MTV_OK:
+        raise MtvError(rc, status_string(rc))
+    return out, lse
+
+
+def mla_tree_verify_noalloc(q: torch.Tensor, kv_pool: torch.Tensor, page_table: torch.Tensor,
+                            seq_lens: torch.Tensor, tree_mask: torch.Tensor, scale: float,
+                            out: torch.Tensor, lse: torch.Tensor, stream=None):
+    """mla_tree_verify without a workspace argument: the library's fixed
+    per-GPU scratch holds the partials (see mla_tree_verify_noalloc). The
+    caller passes preallocated out bf16 [B,N,H,512] and lse float32 [B,N,H];
+    nothing is allocated here either. Returns (out, lse)."""
+    if q.dim() != 4 or page_table.dim() != 2 or kv_pool.dim() != 2:
+        raise ValueError("q must be [B, N, H, 576], page_table [B, max_kv], kv_pool [P, 576]")
+    B, N, H, _ = q.shape
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("q must be on a GPU")
+    P = kv_pool.shape[0]
+    max_kv = page_table.shape[1]
+    _check(q, "q", torch.bfloat16, (B, N, H, 576), dev)
+    _check(kv_pool, "kv_pool", torch.bfloat16, (P, 576), dev)
+    _check(page_table, "page_table", torch.int32, (B, max_kv), dev)
+    _check(seq_lens, "seq_lens", torch.int32, (B,), dev)
+    if tree_mask.dtype not in (torch.int32, getattr(torch, "uint32", torch.int32)):
+        raise TypeError("tree_mask must hold 32-bit words")
+    _check(tree_mask, "tree_mask", tree_mask.dtype, (B, N, (N + 31) // 32), dev)
+    _check(out, "out", torch.bfloat16, (B, N, H, 512), dev)
+    _check(lse, "lse", torch.float32, (B, N, H), dev)
+    shape = make_shape(B, N, H, max_kv, P)
+    lib = load()
+    with torch.cuda.device(dev):
+        rc = lib.mla_tree_verify_noalloc(ctypes.byref(shape), _ptr(q), _ptr(kv_pool), _ptr(page_table),
+                                         _ptr(seq_lens), _ptr(tree_mask), ctypes.c_float(scale),
+                                         _ptr(out), _ptr(lse), _stream_handle(dev, stream))
     if rc != MTV_OK:
         raise MtvError(rc, status_string(rc))
     return out, lse

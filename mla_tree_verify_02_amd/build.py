@@ -12,7 +12,7 @@ LIB_NAME = "libmla_tree_verify.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 SOURCES = [os.path.join(CSRC, "mtv_api.cpp"), os.path.join(CSRC, "mtv_kernels.hip"),
            os.path.join(CSRC, "mtv_tree.hip"), os.path.join(CSRC, "mtv_kv.hip"),
-           os.path.join(CSRC, "mtv_check.hip")]
+           os.path.join(CSRC, "mtv_check.hip"), os.path.join(CSRC, "mtv_noalloc.hip")]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

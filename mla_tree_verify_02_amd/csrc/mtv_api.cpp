@@ -341,6 +341,8 @@ const char* mtv_status_string(int status)
         return "workspace smaller than mla_tree_verify_workspace_size()";
     case MTV_ERR_HIP:
         return "HIP runtime error (no device, or a launch failed)";
+    case MTV_ERR_SCRATCH:
+        return "the call needs more workspace than the no-alloc scratch holds (MTV_NOALLOC_SCRATCH_BYTES)";
     default:
         return "unknown status";
     }
