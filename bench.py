@@ -39,10 +39,12 @@ if ROOT not in sys.path:
 
 METRIC = "achieved HBM GB/s (% of peak) for MLA tree-verify at 64k/185k ctx; µs/layer"
 KERNEL_SOURCE = os.path.join(ROOT, "mla_tree_verify_02_amd", "csrc", "mtv_kernels.hip")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "split_kernel_binary16-ctx65536_traffic.json")
+PROFILE_FILE = os.path.join(ROOT, "profiles", "binary16-ctx65536_counters.json")
 PEAK_GBPS = 8000.0
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+MALL_BYTES = 256 << 20     # MI355X Infinity Cache
 LAYERS = 61
+SWEEP_CONTEXTS = "1024,11264,32768,65536,131072,189440"
 
 
 def log(msg: str) -> None:
@@ -63,17 +65,111 @@ def kernel_source_hash() -> str:
         return hashlib.sha256(f.read()).hexdigest()
 
 
-def measured_traffic():
-    """HBM bytes per split-kernel launch from the committed counter summary, if
-    it was taken on the current kernel source (else None)."""
+def measured_profile():
+    """The committed rocprofv3 summary of the headline workload (kernel trace
+    durations, HBM bytes from FETCH_SIZE/WRITE_SIZE, MFMA busy share), if it
+    was taken on the current kernel source; else None."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(PROFILE_FILE) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
     if t.get("kernel_source_sha256") != kernel_source_hash():
         return None
-    return t.get("hbm_bytes_per_launch")
+    return t
+
+
+SAMPLER_CHILD = r'''
+import json, sys, time
+import amdsmi
+amdsmi.amdsmi_init()
+h = amdsmi.amdsmi_get_processor_handles()[0]
+period = float(sys.argv[1])
+out = open(sys.argv[2], "w")
+def get(fn):
+    try:
+        v = fn()
+        return float(v) if isinstance(v, (int, float)) else None
+    except Exception:
+        return None
+while True:
+    act = {}
+    try:
+        act = amdsmi.amdsmi_get_gpu_activity(h)
+    except Exception:
+        pass
+    rec = {"t": time.time(),
+           "gfx_mhz": get(lambda: amdsmi.amdsmi_get_clock_info(h, amdsmi.AmdSmiClkType.GFX)["clk"]),
+           "mem_mhz": get(lambda: amdsmi.amdsmi_get_clock_info(h, amdsmi.AmdSmiClkType.MEM)["clk"]),
+           "power_w": get(lambda: amdsmi.amdsmi_get_power_info(h)["current_socket_power"]),
+           "gfx_activity_pct": get(lambda: act["gfx_activity"]),
+           "umc_activity_pct": get(lambda: act["umc_activity"])}
+    out.write(json.dumps(rec) + "\n")
+    out.flush()
+    time.sleep(period)
+'''
+
+
+class ClockSampler:
+    """Samples the GPU's graphics and memory clocks, socket power and engine
+    activity (graphics, memory controller) through the amdsmi library, about
+    every `period` seconds, in a child process (so that the bench's own
+    launch loop cannot starve it), while the timed work runs. The analogue of
+    an nvidia-smi probe beside a decode run. Reports None if the library or
+    the device refuses. The summary covers all samples and, separately, the
+    samples taken while the graphics engine was busy."""
+
+    def __init__(self, period=0.05):
+        self.period = period
+        self.proc = None
+        self.path = None
+
+    def start(self):
+        import subprocess
+        import tempfile
+        fd, self.path = tempfile.mkstemp(prefix="mtv_clocks_", suffix=".jsonl")
+        os.close(fd)
+        try:
+            self.proc = subprocess.Popen([sys.executable, "-c", SAMPLER_CHILD, str(self.period), self.path],
+                                         stdout=subprocess.DEVNULL, stderr=subprocess.DEVNULL)
+        except OSError as e:
+            log("clock sampling unavailable: %s" % e)
+            self.proc = None
+        return self
+
+    def stop(self):
+        if self.proc is None:
+            return None
+        self.proc.terminate()
+        try:
+            self.proc.wait(timeout=5)
+        except Exception:
+            self.proc.kill()
+        recs = []
+        try:
+            with open(self.path) as f:
+                for line in f:
+                    try:
+                        recs.append(json.loads(line))
+                    except ValueError:
+                        pass
+            os.unlink(self.path)
+        except OSError:
+            pass
+        if not recs:
+            log("clock sampling returned no samples")
+            return None
+
+        def summary(rs):
+            out = {"samples": len(rs)}
+            for key in ("gfx_mhz", "mem_mhz", "power_w", "gfx_activity_pct", "umc_activity_pct"):
+                v = sorted(r[key] for r in rs if r.get(key) is not None)
+                if v:
+                    out[key] = {"min": v[0], "p50": v[len(v) // 2], "max": v[-1]}
+            return out
+
+        busy = [r for r in recs if (r.get("gfx_activity_pct") or 0) >= 50]
+        return {"period_s": self.period, "all": summary(recs), "gfx_busy": summary(busy) if busy else None}
 
 
 def copy_calibration(mib, torch):
@@ -194,6 +290,28 @@ def other_configs(args, torch, M, I):
     arrays."""
     out = {}
     names = [c.strip() for c in args.configs.split(",") if c.strip()]
+    if "c1" in names:
+        # the tiny chain: 1.3 MB per call, served by the caches and bound by
+        # launch and fixed per-call cost rather than by HBM
+        log("building tiny-chain-ctx1024 (8 rotated sets)")
+        wls = [I.config_workload(1, device="cuda", layer=r) for r in range(8)]
+        ws = None
+        calls = []
+        for wl in wls:
+            c = M.prepare_workload(wl, workspace=ws)
+            ws = c.workspace
+            calls.append(c)
+        sec = time_calls(calls, args.steps, args.warmup, torch)
+        us = time_each_call(calls, args.steps, torch)
+        seq = wls[0].seq_lens_host()
+        b = I.algorithmic_bytes(seq, wls[0].num_nodes, wls[0].num_heads)
+        med = pct(us, 0.5)
+        out["tiny-chain-ctx1024"] = {
+            "us_per_call": {"p10": round(pct(us, 0.1), 2), "p50": round(med, 2), "p90": round(pct(us, 0.9), 2)},
+            "wall_us_per_call": round(sec * 1e6, 2), "bytes_per_call": b,
+            "gbps": round(b / (med * 1e-6) / 1e9, 1), "cache_resident": True}
+        log("tiny-chain-ctx1024: %.2f us/call (events), %.2f us/call (wall)" % (med, sec * 1e6))
+        del calls, wls, ws
     if "c4" in names:
         log("building random64-h64-ctx131072 (2 rotated sets)")
         wls = [I.config_workload(4, device="cuda", layer=r) for r in range(2)]
@@ -259,7 +377,7 @@ def other_configs(args, torch, M, I):
         w = hl.workload
         out_t = torch.empty((w.batch, w.num_nodes, w.num_heads, 512), dtype=torch.bfloat16, device="cuda")
         lse_t = torch.empty((w.batch, w.num_nodes, w.num_heads), dtype=torch.float32, device="cuda")
-        ws_t = torch.empty(M.workspace_size(M.make_shape(w.batch, w.num_nodes, w.num_heads, w.max_kv,
+        ws_t = torch.zeros(M.workspace_size(M.make_shape(w.batch, w.num_nodes, w.num_heads, w.max_kv,
                                                          w.num_slots)), dtype=torch.uint8, device="cuda")
 
         class _Paged:
@@ -468,20 +586,72 @@ def sweep(args, torch, M, I):
             graph.replay()
         torch.cuda.synchronize()
         gstep_s = (time.perf_counter() - t0) / steps
+        # a whole step's rows fit in the 256 MB Infinity Cache only at the
+        # shortest contexts; those figures are cache-served, not HBM-bound
+        mall = LAYERS * b_layer <= MALL_BYTES
         results.append({"context": ctx, "layers": LAYERS, "us_per_layer": round(us_layer, 3),
                         "ms_per_step": round(step_s * 1e3, 4), "gbps": round(gbps, 1),
                         "pct_of_peak": round(100 * gbps / PEAK_GBPS, 2),
-                        "bytes_per_step": LAYERS * b_layer,
+                        "bytes_per_layer": b_layer, "bytes_per_step": LAYERS * b_layer,
+                        "mall_resident": mall,
                         "tokens_per_s_equiv": round(1.0 / step_s, 2),
                         "captured": {"us_per_layer": round(gstep_s / LAYERS * 1e6, 3),
                                      "ms_per_step": round(gstep_s * 1e3, 4),
                                      "gbps": round(b_layer * LAYERS / gstep_s / 1e9, 1),
+                                     "pct_of_peak": round(100 * b_layer * LAYERS / gstep_s / 1e9 / PEAK_GBPS, 2),
                                      "tokens_per_s_equiv": round(1.0 / gstep_s, 2)}})
         log("sweep ctx %d: %.2f us/layer, %.0f GB/s (graph-captured step: %.2f us/layer)"
             % (ctx, us_layer, gbps, gstep_s / LAYERS * 1e6))
         del graph
         del calls
     return results
+
+
+def cpu_per_config(I, threads):
+    """The oracle's time per layer-step on the other configurations, with the
+    same inputs as the GPU lines (built on the GPU, copied to the host):
+    the tiny chain whole; one layer of the 61-layer sweep at 65536 and 189440
+    (x61 extrapolated to a step); the 64 x 64-head call on 4 rows of every
+    64-row group (extrapolated to its 4096 rows); the batch-8 call whole."""
+    import numpy as np
+    from oracle import oracle as O
+
+    def timed(wl, rows=None, min_s=0.3):
+        host = (wl.np_q(), wl.np_kv(), wl.np_page_table(), wl.np_seq_lens(), wl.np_mask())
+        n, t = 0, 0.0
+        while t < min_s or n == 0:
+            t0 = time.perf_counter()
+            O.run(*host, wl.scale, rows=rows, threads=threads)
+            t += time.perf_counter() - t0
+            n += 1
+        return t / n
+
+    res = {}
+    wl = I.config_workload(1, device="cuda")
+    s = timed(wl)
+    res["tiny-chain-ctx1024"] = {"ms_per_layer_step": round(s * 1e3, 3), "rows": 64}
+    for ctx in (65536, 189440):
+        wl = I.config_workload(3, device="cuda", ctx=ctx, layer=0)
+        s = timed(wl, min_s=0.0)
+        res["chain8-ctx%d" % ctx] = {"ms_per_layer": round(s * 1e3, 2), "rows": 64,
+                                     "ms_per_step_61_layers": round(61 * s * 1e3, 1),
+                                     "extrapolated": "one layer timed, x61 for the step"}
+        del wl
+    wl = I.config_workload(4, device="cuda")
+    rng = np.random.default_rng(4)
+    rows = np.concatenate([g0 + rng.choice(64, size=4, replace=False) for g0 in range(0, 4096, 64)])
+    s = timed(wl, rows=rows, min_s=0.0)
+    res["random64-h64-ctx131072"] = {"ms_per_layer_step": round(s * 4096 / len(rows) * 1e3, 1),
+                                     "rows_timed": int(len(rows)),
+                                     "extrapolated": "%d of 4096 rows timed, x%.0f" % (len(rows), 4096 / len(rows))}
+    del wl
+    wl = I.config_workload(5, device="cuda")
+    s = timed(wl, min_s=0.0)
+    res["batch8-loguniform"] = {"ms_per_layer_step": round(s * 1e3, 2), "rows": 512}
+    del wl
+    for k, v in res.items():
+        log("CPU oracle %s: %s" % (k, v))
+    return res
 
 
 def cpu_baseline(wls, call_bytes, I):
@@ -541,7 +711,9 @@ def cpu_baseline(wls, call_bytes, I):
     KM.kv_defrag(pool, table, [65536], [65536])
     defrag_us = (time.perf_counter() - t0) * 1e6
     rows = wls[0].batch * wls[0].num_nodes * wls[0].num_heads
+    per_config = cpu_per_config(I, threads)
     return {"value": round(calls * call_bytes / total / 1e9, 4), "unit": "GB/s",
+            "per_config": per_config,
             "tree_mask_build_us": mask_us,
             "kv_commit_b1_n16_l5_us": round(commit_us, 1),
             "kv_defrag_s65536_us": round(defrag_us, 1),
@@ -551,6 +723,40 @@ def cpu_baseline(wls, call_bytes, I):
                       "cycling over its %d input sets" % (calls, rows, len(wls))}
 
 
+def roofline_entry(hd, achieved, prof):
+    """The dominant kernel against 8 TB/s: algorithmic bytes per launch over
+    the average launch duration by HIP events in this run (achieved, frac);
+    with the committed profile of the same kernel source, also over the
+    kernel-trace average (achieved_trace, frac_trace), the HBM bytes the
+    FETCH_SIZE/WRITE_SIZE counters saw per launch (traffic) and per call
+    (call_traffic, against the call's algorithmic bytes), and the MFMA busy
+    share."""
+    r = {"bound": "hbm", "kernel": "split_kernel",
+         "achieved": round(achieved, 1), "peak": PEAK_GBPS, "unit": "GB/s",
+         "frac": round(achieved / PEAK_GBPS, 4), "traffic": None,
+         "avg_launch_us": round(hd["split_avg_ms"] * 1e3, 3),
+         "bytes_per_launch": hd["split_bytes"], "call_bytes": hd["call_bytes"]}
+    if prof is None:
+        r["profile"] = None
+        return r
+    k = prof["kernels"]["split_kernel"]
+    r["profile"] = os.path.relpath(PROFILE_FILE, ROOT)
+    r["traffic"] = k.get("hbm_bytes_per_dispatch")
+    if r["traffic"]:
+        r["traffic_ratio"] = round(r["traffic"] / hd["split_bytes"], 4)
+    if k.get("trace_avg_us"):
+        a = hd["split_bytes"] / (k["trace_avg_us"] * 1e-6) / 1e9
+        r["trace_avg_us"] = k["trace_avg_us"]
+        r["achieved_trace"] = round(a, 1)
+        r["frac_trace"] = round(a / PEAK_GBPS, 4)
+    call = sum(v.get("hbm_bytes_per_dispatch") or 0 for v in prof["kernels"].values())
+    if call:
+        r["call_traffic"] = call
+        r["call_traffic_ratio"] = round(call / hd["call_bytes"], 4)
+    r["mfma_busy_pct"] = k.get("mfma_busy_pct")
+    return r
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -558,16 +764,19 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=200,
                     help="untimed calls first (about 8 ms of work, so that clocks settle)")
     ap.add_argument("--rotate", type=int, default=8, help="independent input sets cycled over")
-    ap.add_argument("--sweep", default="65536,189440",
+    ap.add_argument("--sweep", default=SWEEP_CONTEXTS,
                     help="contexts of the 61-layer chain8 sweep ('' to skip)")
     ap.add_argument("--sweep-steps", type=int, default=5)
-    ap.add_argument("--configs", default="c4,c5,mask,kv",
-                    help="other configurations to time: c4 (64 nodes x 64 heads, ctx 131072), "
+    ap.add_argument("--configs", default="c1,c4,c5,mask,kv",
+                    help="other configurations to time: c1 (8-node chain, ctx 1024), "
+                         "c4 (64 nodes x 64 heads, ctx 131072), "
                          "c5 (batch 8, mixed lengths, scattered and runs-of-64 layouts), "
                          "mask (the tree-mask build from parent arrays), "
                          "kv (Tier-0 defrag and accepted-path commit); '' for none")
     ap.add_argument("--big-steps", type=int, default=20, help="timed calls of the c4 configuration")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-clocks", action="store_true",
+                    help="skip the amdsmi clock/power sampler (e.g. under a profiler)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="also run a plain copy of MIB MiB (for counter calibration)")
     args = ap.parse_args()
@@ -579,12 +788,19 @@ def main() -> int:
               % (args.gpus, world), file=sys.stderr)
         return 2
 
+    # started before this process touches the GPU; runs until the sweep ends
+    sampler = ClockSampler() if not args.no_clocks else None
+    if sampler is not None:
+        sampler.start()
+
     import torch
 
     import mla_tree_verify_02_amd as M
     from mla_tree_verify_02_amd import inputs as I
 
     if not torch.cuda.is_available():
+        if sampler is not None:
+            sampler.stop()
         print("bench.py needs a GPU", file=sys.stderr)
         return 2
     M.load()
@@ -601,6 +817,7 @@ def main() -> int:
         % (sec * 1e6, value, hd["split_avg_ms"] * 1e3, hd["split_med_ms"] * 1e3, achieved))
 
     sw = sweep(args, torch, M, I)
+    clocks = sampler.stop() if sampler is not None else None
     oc = other_configs(args, torch, M, I)
     cpu = None if args.no_cpu_baseline else cpu_baseline(hd["wls"], hd["call_bytes"], I)
 
@@ -626,12 +843,9 @@ def main() -> int:
                    "plan": hd["plan"]},
         "us_per_layer": round(sec * 1e6, 3),
         "pct_of_peak": round(100 * value / PEAK_GBPS, 2),
-        "roofline": {"bound": "hbm", "kernel": "split_kernel",
-                     "achieved": round(achieved, 1), "peak": PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(achieved / PEAK_GBPS, 4), "traffic": measured_traffic(),
-                     "avg_launch_us": round(hd["split_avg_ms"] * 1e3, 3),
-                     "bytes_per_launch": hd["split_bytes"]},
+        "roofline": roofline_entry(hd, achieved, measured_profile()),
         "call_us": hd["call_us"],
+        "clocks": clocks,
         "context_sweep": sw,
         "other_configs": oc,
         "cpu_baseline": cpu,
