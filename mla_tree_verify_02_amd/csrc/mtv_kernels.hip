@@ -398,28 +398,47 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(Args a, int slots, i
     const int32_t* pt = a.page_table + (int64_t)b * a.max_kv;
     const int maxslot = (int)(a.num_slots - 1);
     const int nwin = (ntiles + kWinTiles - 1) / kWinTiles;
-    auto slot_of = [&](int p) -> int {
-        int64_t v;
-        if constexpr (kPaged) {
-            const int t0 = S - N;
-            if (p < t0) {
-                const int pg = min(p / a.page_size, a.max_pages - 1);
-                v = (int64_t)a.prefix_pages[(int64_t)b * a.max_pages + pg] * a.page_size +
-                    (p - (p / a.page_size) * a.page_size);
-            } else {
-                v = a.tree_slots[(int64_t)b * N + (p - t0)];
-            }
-        } else {
-            v = pt[p];
-        }
-        return (int)(v < 0 ? 0 : (v > maxslot ? maxslot : v));
-    };
     auto stage = [&](int w) {
         const int n = min(ntiles * kTileKeys - w * kWinKeys, kWinKeys);
         if constexpr (kPaged) {
+            // Hybrid layout: a prefix position p takes page p / page_size of
+            // its row (a page number past the row reads the last entry) plus
+            // p % page_size; a tree position takes its tree_slots entry. Every
+            // entry of this thread's positions is loaded first, so the window
+            // costs one round trip (a shift for a power-of-two page size).
+            constexpr int kPer = kWinKeys / kThreads;
+            const int ps = a.page_size;
+            const bool pow2 = (ps & (ps - 1)) == 0;
+            const int sh = __builtin_ctz((unsigned)ps);
+            const int t0 = S - N;
+            const int32_t* prow = a.prefix_pages + (int64_t)b * a.max_pages;
+            const int32_t* trow = a.tree_slots + (int64_t)b * N;
+            int32_t e[kPer];
+            int off[kPer];
+#pragma unroll
+            for (int j = 0; j < kPer; ++j) {
+                e[j] = 0;
+                off[j] = -1;  // -1: a tree position (no page arithmetic)
+                if (j * kThreads < n) {  // uniform
+                    const int p = min(k0 + w * kWinKeys + min(tid + j * kThreads, n - 1), S - 1);
+                    const int32_t* src = trow + (p - t0);
+                    if (p < t0) {
+                        const int pg = pow2 ? (p >> sh) : p / ps;
+                        off[j] = p - pg * ps;
+                        src = prow + min(pg, a.max_pages - 1);
+                    }
+                    e[j] = *src;
+                }
+            }
             int* dst = s_idx[w & 1];
-            for (int i = tid; i < n; i += kThreads)
-                dst[i] = slot_of(min(k0 + w * kWinKeys + i, S - 1));
+#pragma unroll
+            for (int j = 0; j < kPer; ++j) {
+                const int i = tid + j * kThreads;
+                if (i < n) {
+                    const int64_t v = off[j] >= 0 ? (int64_t)e[j] * ps + off[j] : (int64_t)e[j];
+                    dst[i] = (int)(v < 0 ? 0 : (v > maxslot ? maxslot : v));  // clamped to the pool
+                }
+            }
         } else {
             // Table words go straight to LDS (direct loads, no registers and
             // no wait here): the vmcnt waits of the tile loop, which only

@@ -181,3 +181,31 @@ def test_graph_capture_paged():
         torch.cuda.synchronize()
         assert torch.equal(out.view(torch.int16), ref_o.view(torch.int16))
         assert torch.equal(lse.view(torch.int32), ref_l.view(torch.int32))
+
+
+@pytest.mark.parametrize("page_size", [48, 100])
+def test_page_size_not_a_power_of_two(oracle_mod, page_size):
+    # page numbers by division rather than a shift; ragged last pages
+    wl = I.make_workload(batch=2, num_nodes=9, num_heads=8, prefix_lens=[5000, 777],
+                         num_slots=16384, tree="random", max_depth=4, config_id=25, device="cuda")
+    hl = I.hybrid_layout(wl, page_size, seed=page_size)
+    w = hl.workload
+    table = oracle_expand(w, hl.prefix_pages, hl.tree_slots, page_size)
+    out, lse = check_bitwise(w, hl.prefix_pages, hl.tree_slots, page_size, table)
+    check_vs_oracle(oracle_mod, w, table, out, lse, label=f"paged{page_size}")
+
+
+def test_long_slices_restage_paged_window(oracle_mod):
+    """2048 rows over ~40k keys leave slices of more than one 4096-position
+    window, so the hybrid layout's index staging runs again inside the tile
+    loop; bit for bit equal to the per-token call on the expanded table."""
+    wl = I.make_workload(batch=1, num_nodes=64, num_heads=32, prefix_lens=[40000], num_slots=65536,
+                         tree="random", max_depth=8, config_id=107, device="cuda", q_gain=4.0)
+    plan = M.plan_query(M.make_shape(1, 64, 32, wl.max_kv, wl.num_slots), 256)
+    assert plan["chunk"] > 4096, plan
+    hl = I.hybrid_layout(wl, 64, seed=5)
+    w = hl.workload
+    table = oracle_expand(w, hl.prefix_pages, hl.tree_slots, 64)
+    out, lse = check_bitwise(w, hl.prefix_pages, hl.tree_slots, 64, table)
+    rows = np.unique(np.r_[0, 2047, np.random.default_rng(3).choice(2048, 40, replace=False)])
+    check_vs_oracle(oracle_mod, w, table, out, lse, rows=rows, label="paged long slices")
