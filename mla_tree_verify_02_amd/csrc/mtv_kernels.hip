@@ -488,8 +488,10 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(Args a, int slots, i
     }
     // Page indices of the rows this lane gathers for a tile, read from the ring
     // one tile ahead of the gathers that use them (nothing consumes them before
-    // then, so the LDS latency stays off the tile's path). Each wave reads only
-    // the words its own lanes loaded, so the vmcnt waits alone order them.
+    // then, so the LDS latency stays off the tile's path). A wave's words were
+    // loaded (or, with hybrid paging, written) by other waves' lanes, so what
+    // orders them is each loader's vmcnt wait followed by a barrier: the one
+    // before the first gathers for window 0, the tile barriers for later ones.
     auto load_idx = [&](int t, int* out) {
         const int* tidx = &s_idx[(t / kWinTiles) & 1][(t % kWinTiles) * kTileKeys + wave * kKeysPerWave];
 #pragma unroll
