@@ -65,7 +65,7 @@ extern "C" {
 /* Size of the fixed device scratch that mla_tree_verify_noalloc uses in
  * place of a caller workspace (one copy per GPU, held until the process
  * ends). */
-#define MTV_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+#define MTV_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
 
 /*
  * Problem shape. All fields are host values.
@@ -85,7 +85,8 @@ typedef struct {
 
 /*
  * Bytes of device workspace mla_tree_verify needs for `shape` on the current
- * device (the split plan depends on the device's compute-unit count). Returns 0
+ * device (the split plan depends on the device's compute-unit count); the same
+ * size serves mla_tree_verify_paged and the splitkv/combine pair. Returns 0
  * if the shape is invalid. Host-only; never synchronises.
  */
 size_t mla_tree_verify_workspace_size(const mtv_shape* shape);
@@ -348,8 +349,9 @@ int mtv_check_inputs(const mtv_shape* shape,
  * Limit: a call whose mla_tree_verify_workspace_size(shape) exceeds
  * MTV_NOALLOC_SCRATCH_BYTES returns MTV_ERR_SCRATCH and enqueues nothing
  * (compare the two beforehand to know). On a 256-CU MI355X one sequence of
- * up to 16,384 query rows (N * H) fits at any context (about 17 MB), as do
- * batches of up to 128 sequences of 8 nodes x 8 heads, or up to 64 of 16 x 8.
+ * up to 32,768 query rows (N * H) fits at any context (at most about 34 MB),
+ * as do batches of up to 759 sequences of 8 nodes x 8 heads, or up to 380 of
+ * 16 x 8.
  *
  * Sharing: every call on one GPU uses that GPU's one array, which keeps the
  * last call's contents (nothing in it needs clearing: a call writes every word
@@ -377,7 +379,11 @@ const char* mtv_status_string(int status);
  * key slices per sequence (*splits), keys per slice (*chunk, a multiple of 32)
  * and 64-row groups per sequence (*row_groups). Batches of other lengths are
  * sliced on the device from seq_lens with the same rule (slices of one size
- * for the whole batch, sized from its total key count). Host-only arithmetic.
+ * for the whole batch, sized from its total key count). This is the plan of
+ * the per-token-table calls: from 16 row groups and 128 tiles (4096 keys) per
+ * slice on, two row groups share a split workgroup and the slots per row group
+ * double; mla_tree_verify_paged always runs one row group per workgroup, so
+ * its slicing can differ. Host-only arithmetic.
  * Returns MTV_OK, MTV_ERR_NULL or MTV_ERR_SHAPE.
  */
 int mtv_plan_query(const mtv_shape* shape, int num_cus, int* splits, int* chunk, int* row_groups);

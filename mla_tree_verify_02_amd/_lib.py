@@ -18,7 +18,7 @@ from .build import LIB_PATH
 MTV_OK = 0
 STATUS_NAMES = {0: "MTV_OK", -1: "MTV_ERR_NULL", -2: "MTV_ERR_SHAPE", -3: "MTV_ERR_ALIGN",
                 -4: "MTV_ERR_WORKSPACE", -5: "MTV_ERR_HIP", -6: "MTV_ERR_SCRATCH"}
-NOALLOC_SCRATCH_BYTES = 32 << 20  # MTV_NOALLOC_SCRATCH_BYTES
+NOALLOC_SCRATCH_BYTES = 64 << 20  # MTV_NOALLOC_SCRATCH_BYTES
 EXPORTED = ("mla_tree_verify", "mla_tree_verify_workspace_size", "mtv_status_string",
             "mtv_plan_query", "mla_tree_verify_splitkv", "mla_tree_verify_combine",
             "mla_tree_mask_build", "mla_kv_commit", "mla_kv_defrag", "mla_tree_verify_paged",

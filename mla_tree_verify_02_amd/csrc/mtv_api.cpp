@@ -1,6 +1,7 @@
 // Host side of the C ABI: argument validation, the split plan, workspace
 // layout and the two launches. Never allocates, frees or synchronises.
 #include <atomic>
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 
@@ -55,13 +56,15 @@ size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 // is longer than the others. The kernels derive c and each slice's sequence
 // from seq_lens on the device; the host only bounds the slice count for the
 // grid and the workspace.
-mtv::Plan make_plan(const mtv_shape& s, int cus)
+mtv::Plan make_plan_rb(const mtv_shape& s, int cus, int rb)
 {
     mtv::Plan p{};
     p.rows = s.num_nodes * s.num_heads;
     p.cus = cus;
     p.row_groups = (p.rows + mtv::kRowsPerGroup - 1) / mtv::kRowsPerGroup;
-    int64_t slots = ((int64_t)cus + p.row_groups - 1) / p.row_groups;
+    p.rb = rb;
+    const int wg_groups = (p.row_groups + rb - 1) / rb;
+    int64_t slots = ((int64_t)cus + wg_groups - 1) / wg_groups;
     if (slots < 1)
         slots = 1;
     p.slots = (int)slots;
@@ -89,6 +92,26 @@ mtv::Plan make_plan(const mtv_shape& s, int cus)
     return p;
 }
 
+// Many rows over long slices make the call MFMA-bound: then two row groups
+// share each split workgroup (two 16-row blocks per wave), which halves the
+// LDS operand reads per MFMA and the tile gathers per row. That form costs
+// about 34 us more per call (its rare-rescale path keeps spill space, set up
+// by every wave) and saves about 0.37 us per tile of a slice (measured on
+// 64 x 64 heads at 131072 keys and on 16 and 32 row groups at 32768-65536
+// keys), so it is taken only from 16 row groups and 128 tiles per slice.
+// Per-token tables only: the hybrid layout's index staging leaves that form
+// no registers to spare.
+mtv::Plan make_plan(const mtv_shape& s, int cus, bool paged)
+{
+    const int row_groups = (s.num_nodes * s.num_heads + mtv::kRowsPerGroup - 1) / mtv::kRowsPerGroup;
+    if (!paged && row_groups >= mtv::kRB2MinRowGroups) {
+        const mtv::Plan p2 = make_plan_rb(s, cus, 2);
+        if (p2.single_c >= mtv::kRB2MinTiles)
+            return p2;
+    }
+    return make_plan_rb(s, cus, 1);
+}
+
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
 
 }  // namespace
@@ -102,7 +125,8 @@ size_t mla_tree_verify_workspace_size(const mtv_shape* shape)
     int cus = current_cu_count();
     if (cus <= 0)
         cus = 256;  // no device visible: size for a full MI355X
-    return make_plan(*shape, cus).bytes;
+    // one workspace serves both layouts
+    return std::max(make_plan(*shape, cus, false).bytes, make_plan(*shape, cus, true).bytes);
 }
 
 int mtv_plan_query(const mtv_shape* shape, int num_cus, int* splits, int* chunk, int* row_groups)
@@ -111,7 +135,7 @@ int mtv_plan_query(const mtv_shape* shape, int num_cus, int* splits, int* chunk,
         return MTV_ERR_NULL;
     if (!shape_ok(*shape) || num_cus < 1)
         return MTV_ERR_SHAPE;
-    const mtv::Plan p = make_plan(*shape, num_cus);
+    const mtv::Plan p = make_plan(*shape, num_cus, false);
     *splits = p.splits;
     *chunk = p.chunk;
     *row_groups = p.row_groups;
@@ -168,7 +192,7 @@ int run(int phases, const mtv_shape* shape, const void* q, const void* kv_pool,
     const int cus = current_cu_count();
     if (cus <= 0)
         return MTV_ERR_HIP;
-    const mtv::Plan plan = make_plan(*shape, cus);
+    const mtv::Plan plan = make_plan(*shape, cus, paged);
     if (workspace_bytes < plan.bytes)
         return MTV_ERR_WORKSPACE;
 

@@ -13,14 +13,17 @@ constexpr int kDqk = 576;          // key / absorbed query width
 constexpr int kDv = 512;           // value width (the latent)
 constexpr int kRowBytes = kDqk * 2;
 constexpr int kTileKeys = 32;      // keys per LDS tile
-constexpr int kRowsPerGroup = 64;  // query rows per split workgroup (4 waves x 16)
+constexpr int kRowsPerGroup = 64;  // query rows per row group (4 waves x 16)
+constexpr int kRB2MinRowGroups = 16;  // two row groups per split workgroup from this many
+constexpr int kRB2MinTiles = 128;     // ... and from this many tiles per slice
 
 // How one call is cut into workgroups. Depends only on host values.
 struct Plan {
     int rows;          // R = N * H query rows per sequence
     int cus;           // compute units of the device the plan is for
     int row_groups;    // ceil(R / 64)
-    int slots;         // G: target key slices per row group over the whole batch
+    int rb;            // row groups per split workgroup (16-row blocks per wave): 1 or 2
+    int slots;         // G: target key slices per split workgroup group over the whole batch
     int max_slices;    // G + B: bound on the slices of all sequences together
     int single_c;      // tiles per slice of a batch of one sequence (from max_kv)
     int splits;        // slices per sequence when every sequence holds max_kv keys

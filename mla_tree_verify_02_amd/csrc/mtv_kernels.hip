@@ -274,11 +274,19 @@ __device__ __forceinline__ void slicing(const Args& a, int slots, int single_c, 
 // (slot = prefix_pages[b][p / page_size] * page_size + p % page_size) and the
 // N tree positions through a per-token list (slot = tree_slots[b][p - (S - N)]).
 // The two differ only in the index staging below.
-template <bool kPaged>
+//
+// kRB is the number of 16-row blocks per wave: 1 (64 rows per workgroup) or 2
+// (128 rows: every K and V^T operand read from LDS feeds two MFMAs, and each
+// gathered tile serves twice the rows; for MFMA-bound calls with many rows).
+// Workgroup group g covers the 64-row groups kRB*g .. kRB*g + kRB - 1, and row
+// block rb of wave w holds rows 64 (kRB g + rb) + 16 w .. + 15, so partial
+// results keep the one-row-group layout the combine reads.
+template <bool kPaged, int kRB>
 __global__ __launch_bounds__(kThreads, 1) void split_kernel(Args a, int slots, int single_c,
                                                             int max_slices, int row_groups,
                                                             float scale_log2)
 {
+    static_assert(kRB == 1 || kRB == 2, "one or two row blocks per wave");
     __shared__ __attribute__((aligned(16))) char s_kv[kStages * kTileBytes];
     __shared__ int s_idx[2][kWinKeys];  // page indices, two windows of 128 tiles
 
@@ -300,13 +308,14 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(Args a, int slots, i
     // sequence is laid out by the host bound (its exact slice count for
     // max_kv keys), so the mapping does not wait for seq_lens.
     const int L = blockIdx.x;
-    const int items = (a.batch == 1 ? max_slices : (int)nslices) * row_groups;
-    const int per_xcd = xcd_block(items, row_groups);
+    const int wg_groups = (row_groups + kRB - 1) / kRB;
+    const int items = (a.batch == 1 ? max_slices : (int)nslices) * wg_groups;
+    const int per_xcd = xcd_block(items, wg_groups);
     const int item = (L & 7) * per_xcd + (L >> 3);
     if ((L >> 3) >= per_xcd || item >= items)
         return;  // the whole workgroup (every value above is uniform)
-    const int gslice = item / row_groups;
-    const int grp = item - gslice * row_groups;
+    const int gslice = item / wg_groups;
+    const int grp = item - gslice * wg_groups;  // workgroup group: row groups kRB*grp ..
     const int tid = threadIdx.x;
 
     // The sequence b holding global slice gslice, its slice index there and
@@ -320,14 +329,16 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(Args a, int slots, i
         // so that the combine can merge every slice the host planned for
         // max_kv without waiting for seq_lens (stale slots would hold another
         // call's values).
-        const size_t pz = (size_t)grp * max_slices + gslice;
-        if (tid < kRowsPerGroup) {
-            float2* pm = (float2*)a.part_ml + pz * kRowsPerGroup + tid;
-            *pm = make_float2(-INFINITY, 0.f);
+        for (int rg = grp * kRB; rg < min(grp * kRB + kRB, row_groups); ++rg) {
+            const size_t pz = (size_t)rg * max_slices + gslice;
+            if (tid < kRowsPerGroup) {
+                float2* pm = (float2*)a.part_ml + pz * kRowsPerGroup + tid;
+                *pm = make_float2(-INFINITY, 0.f);
+            }
+            uint4* po = (uint4*)((__bf16*)a.part_o + pz * (size_t)(kRowsPerGroup * kPartRowElems));
+            for (int i = tid; i < kRowsPerGroup * kPartRowElems * 2 / 16; i += kThreads)
+                po[i] = uint4{0u, 0u, 0u, 0u};
         }
-        uint4* po = (uint4*)((__bf16*)a.part_o + pz * (size_t)(kRowsPerGroup * kPartRowElems));
-        for (int i = tid; i < kRowsPerGroup * kPartRowElems * 2 / 16; i += kThreads)
-            po[i] = uint4{0u, 0u, 0u, 0u};
         return;  // the whole workgroup
     }
     if (__builtin_expect(a.batch > 1 && a.batch <= kWaveBatch, 0)) {
@@ -452,23 +463,28 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(Args a, int slots, i
     };
     stage(0);
 
-    // This lane's query row: fragments of Q as the B operand of S^T = K.Q^T.
-    const int row = grp * kRowsPerGroup + wave * 16 + rl;
-    const bool row_ok = row < R;
-    const __bf16* qrow = (const __bf16*)a.q + ((int64_t)b * R + (row_ok ? row : 0)) * kDqk;
-    bf16x8 qf[kKSteps];
-#pragma unroll
-    for (int s = 0; s < kKSteps; ++s) {
-        bf16x8 v = *(const bf16x8*)(qrow + (4 * s + lg) * 8);
-        if (!row_ok)
-            v = bf16x8{};
-        qf[s] = v;
-    }
-    const int node = (row_ok ? row : 0) / H;
+    // This lane's query row in each row block: fragments of Q as the B operand
+    // of S^T = K.Q^T, and the tree-mask words of the row's node.
     const int W = (N + 31) >> 5;
-    const uint32_t* mrow = a.tree_mask + ((int64_t)b * N + node) * W;
-    const uint32_t mw0 = mrow[0];
-    const uint32_t mw1 = W > 1 ? mrow[1] : 0u;
+    bf16x8 qf[kRB][kKSteps];
+    uint32_t mw0[kRB], mw1[kRB];
+#pragma unroll
+    for (int rb = 0; rb < kRB; ++rb) {
+        const int row = (grp * kRB + rb) * kRowsPerGroup + wave * 16 + rl;
+        const bool row_ok = row < R;
+        const __bf16* qrow = (const __bf16*)a.q + ((int64_t)b * R + (row_ok ? row : 0)) * kDqk;
+#pragma unroll
+        for (int s = 0; s < kKSteps; ++s) {
+            bf16x8 v = *(const bf16x8*)(qrow + (4 * s + lg) * 8);
+            if (!row_ok)
+                v = bf16x8{};
+            qf[rb][s] = v;
+        }
+        const int node = (row_ok ? row : 0) / H;
+        const uint32_t* mrow = a.tree_mask + ((int64_t)b * N + node) * W;
+        mw0[rb] = mrow[0];
+        mw1[rb] = W > 1 ? mrow[1] : 0u;
+    }
     const int tree0 = S - N;  // first key position holding a tree node
 
     const uint32_t lds0 = (uint32_t)(uintptr_t)(LDS_AS char*)s_kv;
@@ -478,14 +494,30 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(Args a, int slots, i
     // wave-wide 1024-byte loads; load j puts lane l's 16 bytes at row
     // kl = (64j + l) / 72, slot (64j + l) % 72, which holds logical chunk
     // slot ^ swz(kl). Every aligned 8-lane group covers one full 128-byte band.
+    // With two row blocks the pair is packed in one register (byte offset in
+    // the low 16 bits) and passed through an empty asm statement once per tile
+    // (opaque_plan), so that the unpacking and the row addresses derived from
+    // it are formed in the loop rather than kept live across it: that leaves
+    // room for the second block's Q and O.
     int gkl[kLoadsPerWave];
     int gco[kLoadsPerWave];
+    int gpk[kLoadsPerWave];
 #pragma unroll
     for (int j = 0; j < kLoadsPerWave; ++j) {
         const int z = j * 64 + lane;
         gkl[j] = z / kChunks;
         gco[j] = ((z - gkl[j] * kChunks) ^ swz(gkl[j])) * 16;
+        gpk[j] = gco[j] | (gkl[j] << 16);
     }
+    auto g_kl = [&](int j) { return kRB == 1 ? gkl[j] : gpk[j] >> 16; };
+    auto g_co = [&](int j) { return kRB == 1 ? gco[j] : gpk[j] & 0xffff; };
+    auto opaque_plan = [&]() {
+        if constexpr (kRB > 1)
+            asm volatile(""
+                         : "+v"(gpk[0]), "+v"(gpk[1]), "+v"(gpk[2]), "+v"(gpk[3]), "+v"(gpk[4]),
+                           "+v"(gpk[5]), "+v"(gpk[6]), "+v"(gpk[7]), "+v"(gpk[8]));
+    };
+    static_assert(kLoadsPerWave == 9, "opaque_plan names every load of the plan");
     // Page indices of the rows this lane gathers for a tile, read from the ring
     // one tile ahead of the gathers that use them (nothing consumes them before
     // then, so the LDS latency stays off the tile's path). A wave's words were
@@ -496,14 +528,14 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(Args a, int slots, i
         const int* tidx = &s_idx[(t / kWinTiles) & 1][(t % kWinTiles) * kTileKeys + wave * kKeysPerWave];
 #pragma unroll
         for (int j = 0; j < kLoadsPerWave; ++j)
-            out[j] = min(max(tidx[gkl[j]], 0), maxslot);  // slots clamped to the pool
+            out[j] = min(max(tidx[g_kl(j)], 0), maxslot);  // slots clamped to the pool
     };
     auto issue = [&](int t, const int* idx) {
         const uint32_t dst = lds0 + (uint32_t)((t % kStages) * kTileBytes +
                                                wave * (kKeysPerWave * kRowBytes));
 #pragma unroll
         for (int j = 0; j < kLoadsPerWave; ++j)
-            gather16_to_lds(kv + (int64_t)idx[j] * kRowBytes + gco[j], dst + j * 1024);
+            gather16_to_lds(kv + (int64_t)idx[j] * kRowBytes + g_co(j), dst + j * 1024);
     };
 
     // Per-lane LDS byte offsets inside a tile buffer; everything else is an
@@ -524,10 +556,12 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(Args a, int slots, i
     for (int qd = 0; qd < 4; ++qd)
         voff[qd] = vkey * kRowBytes + 16 * ((2 * qd + vsel) ^ fv) + (rl & 1) * 8;
 
-    f32x4 o[kColBlocks];
+    f32x4 o[kRB][kColBlocks];
 #pragma unroll
-    for (int cb = 0; cb < kColBlocks; ++cb)
-        o[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int rb = 0; rb < kRB; ++rb)
+#pragma unroll
+        for (int cb = 0; cb < kColBlocks; ++cb)
+            o[rb][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
     // Reference max m_ref (log2 units, shared by the row's four lanes) and this
     // lane's share of the running sum. Weights are 2^(x - m_ref); the reference
     // is raised only when a tile's max exceeds it by more than kSlack, so weights
@@ -535,8 +569,12 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(Args a, int slots, i
     // steady-state loop (at the first tile and whenever scores jump by more than
     // kSlack), so the hot loop touches O only through MFMA accumulation.
     constexpr float kSlack = 16.0f;
-    float m_ref = -INFINITY;
-    float l_run = 0.f;
+    float m_ref[kRB], l_run[kRB];
+#pragma unroll
+    for (int rb = 0; rb < kRB; ++rb) {
+        m_ref[rb] = -INFINITY;
+        l_run[rb] = 0.f;
+    }
 
     // Q fragments and mask words must be in registers, and the first index
     // window in LDS, before the gathers start: past this point the only
@@ -556,7 +594,10 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(Args a, int slots, i
     // K-operand reads per group (double-buffered): groups of 4 give 9 groups,
     // one per row gather of tile t+2 (measured against groups of 6 with the
     // last three gathers in the P.V: 2 % faster on 128 rows, 3-5 % on the
-    // MFMA-bound 64 x 64 heads, same elsewhere, bit-identical)
+    // MFMA-bound 64 x 64 heads, same elsewhere, bit-identical). With two row
+    // blocks, groups of 4 K reads and 4 V column blocks were measured against
+    // 1, 2 and 4 of each on the 64 x 64 heads: 2-3 % ahead of (2, 2), 25 %
+    // ahead of single K reads.
     constexpr int kKGroup = 4;
     constexpr int kKReads = 2 * kKSteps;  // 36 per tile (two key blocks)
     constexpr int kVGroup = 4;            // column blocks per V-operand group
@@ -581,12 +622,71 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(Args a, int slots, i
             load_idx(t + 2, idx_n);
     };
 
+    // Scores of a tile that reaches the tree block or the end of the sequence
+    // get the tree bitmask and the end of the sequence (-inf where hidden).
+    auto mask_tail = [&](int base, float (&x)[kRB][8]) {
+        if (base + kTileKeys > tree0) {
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const int p = base + (k >> 2) * 16 + 4 * lg + (k & 3);
+                const int j = p - tree0;
+#pragma unroll
+                for (int rb = 0; rb < kRB; ++rb) {
+                    bool vis = p < tree0;
+                    if (p >= tree0 && p < S)
+                        vis = (((j < 32) ? mw0[rb] : mw1[rb]) >> (j & 31)) & 1u;
+                    if (!vis)
+                        x[rb][k] = -INFINITY;
+                }
+            }
+        }
+    };
+
     int t = 0;
     next_tile(0);
+    if constexpr (kRB > 1) {
+        // Every row's first reference comes from tile 0's scores, computed
+        // once here: leaving the loop to raise a reference makes the compiler
+        // move O and much else through memory, and at tile 0 every wave would.
+        // The result is that of the raise path (O and the sum are still zero).
+        const char LDS_AS* kb0 = (const char LDS_AS*)s_kv + koff0;  // tile 0: buffer 0
+        const char LDS_AS* kb1 = (const char LDS_AS*)s_kv + koff1;
+        f32x4 sacc[kRB][2];
+#pragma unroll
+        for (int rb = 0; rb < kRB; ++rb)
+            sacc[rb][0] = sacc[rb][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int n = 0; n < kKReads; ++n) {
+            const int s = n >> 1;
+            const bf16x8 kfv =
+                *(const bf16x8 LDS_AS*)(((s & 1) ? kb1 : kb0) + (n & 1) * 16 * kRowBytes + 128 * (s >> 1));
+#pragma unroll
+            for (int rb = 0; rb < kRB; ++rb)
+                sacc[rb][n & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kfv, qf[rb][s], sacc[rb][n & 1], 0, 0, 0);
+        }
+        float x0[kRB][8];
+#pragma unroll
+        for (int rb = 0; rb < kRB; ++rb)
+#pragma unroll
+            for (int k = 0; k < 8; ++k)
+                x0[rb][k] = sacc[rb][k >> 2][k & 3] * scale_log2;
+        mask_tail(k0, x0);
+#pragma unroll
+        for (int rb = 0; rb < kRB; ++rb) {
+            float m = x0[rb][0];
+#pragma unroll
+            for (int k = 1; k < 8; ++k)
+                m = fmaxf(m, x0[rb][k]);
+            m = fmaxf(m, __shfl_xor(m, 16));
+            m = fmaxf(m, __shfl_xor(m, 32));
+            m_ref[rb] = m;
+        }
+    }
     while (true) {
-        float x[8];
-        float mt;
+        float x[kRB][8];
+        float mt[kRB];
         for (;;) {
+            opaque_plan();
             const char LDS_AS* buf = (const char LDS_AS*)s_kv + (t % kStages) * kTileBytes;
             const char LDS_AS* kb0 = buf + koff0;
             const char LDS_AS* kb1 = buf + koff1;
@@ -613,7 +713,10 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(Args a, int slots, i
 #pragma unroll
             for (int j = 0; j < kKGroup; ++j)
                 kf[0][j] = *(const bf16x8 LDS_AS*)kptr(j);
-            f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+            f32x4 sacc[kRB][2];
+#pragma unroll
+            for (int rb = 0; rb < kRB; ++rb)
+                sacc[rb][0] = sacc[rb][1] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int g = 0; g < kKReads / kKGroup; ++g) {
                 if (g + 1 < kKReads / kKGroup) {
@@ -623,12 +726,14 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(Args a, int slots, i
                             *(const bf16x8 LDS_AS*)kptr((g + 1) * kKGroup + j);
                 }
                 if (g < kLoadsPerWave)
-                    gather16_to_lds(kv + (int64_t)idx_n[g] * kRowBytes + gco[g], gdst + g * 1024);
+                    gather16_to_lds(kv + (int64_t)idx_n[g] * kRowBytes + g_co(g), gdst + g * 1024);
 #pragma unroll
                 for (int j = 0; j < kKGroup; ++j) {
                     const int n = g * kKGroup + j;
-                    sacc[n & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                        kf[g & 1][j], qf[n >> 1], sacc[n & 1], 0, 0, 0);
+#pragma unroll
+                    for (int rb = 0; rb < kRB; ++rb)
+                        sacc[rb][n & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            kf[g & 1][j], qf[rb][n >> 1], sacc[rb][n & 1], 0, 0, 0);
                 }
             }
 
@@ -643,56 +748,53 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(Args a, int slots, i
             }
 
 #pragma unroll
-            for (int k = 0; k < 8; ++k)
-                x[k] = sacc[k >> 2][k & 3] * scale_log2;
+            for (int rb = 0; rb < kRB; ++rb)
+#pragma unroll
+                for (int k = 0; k < 8; ++k)
+                    x[rb][k] = sacc[rb][k >> 2][k & 3] * scale_log2;
 
             // keep one group of K-operand reads in flight ahead of the Q.K^T MFMAs
             __builtin_amdgcn_sched_group_barrier(0x100, kKGroup, 0);
 #pragma unroll
             for (int i = 0; i < kKReads - kKGroup; ++i) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, kRB, 0);
                 __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
             }
-            __builtin_amdgcn_sched_group_barrier(0x008, kKGroup, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, kKGroup * kRB, 0);
             __builtin_amdgcn_sched_group_barrier(0x100, 2 * kVGroup, 0);
-            if (base + kTileKeys > tree0) {
-                // tail tile: tree bitmask and the end of the sequence
-#pragma unroll
-                for (int k = 0; k < 8; ++k) {
-                    const int p = base + (k >> 2) * 16 + 4 * lg + (k & 3);
-                    bool vis = p < tree0;
-                    if (p >= tree0 && p < S) {
-                        const int j = p - tree0;
-                        vis = (((j < 32) ? mw0 : mw1) >> (j & 31)) & 1u;
-                    }
-                    if (!vis)
-                        x[k] = -INFINITY;
-                }
-            }
+            mask_tail(base, x);
 
-            // This lane's largest score; whether any exceeds the reference by
-            // more than kSlack decides the (rare) rescale. The row's exact max
-            // over its four lanes is only formed on that path.
-            mt = x[0];
+            // This lane's largest score per row; whether any exceeds its
+            // reference by more than kSlack decides the (rare) rescale. A row's
+            // exact max over its four lanes is only formed on that path.
+            bool raise = false;
 #pragma unroll
-            for (int k = 1; k < 8; ++k)
-                mt = fmaxf(mt, x[k]);
-            if (__builtin_amdgcn_ballot_w64(mt > m_ref + kSlack) != 0)
+            for (int rb = 0; rb < kRB; ++rb) {
+                mt[rb] = x[rb][0];
+#pragma unroll
+                for (int k = 1; k < 8; ++k)
+                    mt[rb] = fmaxf(mt[rb], x[rb][k]);
+                raise = raise || mt[rb] > m_ref[rb] + kSlack;
+            }
+            if (__builtin_amdgcn_ballot_w64(raise) != 0)
                 break;  // raise the reference first (outside this loop)
 
-            const float mr = (m_ref == -INFINITY) ? 0.f : m_ref;
-            bf16x8 pb;
-            float psum = 0.f;
+            bf16x8 pb[kRB];
 #pragma unroll
-            for (int k = 0; k < 8; ++k) {
-                // hardware 2^x (v_exp_f32): the argument lies in [-inf, kSlack];
-                // results below the smallest normal float (weights under 2^-126
-                // of the reference) flush to zero
-                const float pk = __builtin_amdgcn_exp2f(x[k] - mr);
-                psum += pk;
-                pb[k] = (__bf16)pk;
+            for (int rb = 0; rb < kRB; ++rb) {
+                const float mr = (m_ref[rb] == -INFINITY) ? 0.f : m_ref[rb];
+                float psum = 0.f;
+#pragma unroll
+                for (int k = 0; k < 8; ++k) {
+                    // hardware 2^x (v_exp_f32): the argument lies in [-inf,
+                    // kSlack]; results below the smallest normal float (weights
+                    // under 2^-126 of the reference) flush to zero
+                    const float pk = __builtin_amdgcn_exp2f(x[rb][k] - mr);
+                    psum += pk;
+                    pb[rb][k] = (__bf16)pk;
+                }
+                l_run[rb] += psum;
             }
-            l_run += psum;
 
             // O^T[col][row] += V^T[col][key] . P^T[key][row]; the k order of the
             // MFMA is keys (4lg..4lg+3, 16+4lg..16+4lg+3), matching pb.
@@ -715,24 +817,26 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(Args a, int slots, i
                     constexpr int kVGs = kColBlocks / kVGroup;
 #pragma unroll
                     for (int j = kKGroups + g * kRest / kVGs; j < kKGroups + (g + 1) * kRest / kVGs; ++j)
-                        gather16_to_lds(kv + (int64_t)idx_n[j] * kRowBytes + gco[j], gdst + j * 1024);
+                        gather16_to_lds(kv + (int64_t)idx_n[j] * kRowBytes + g_co(j), gdst + j * 1024);
                 }
 #pragma unroll
                 for (int c = 0; c < kVGroup; ++c) {
                     const int cb = g * kVGroup + c;
                     const bf16x8 va = __builtin_shufflevector(
                         vt[g & 1][2 * c], vt[g & 1][2 * c + 1], 0, 1, 2, 3, 4, 5, 6, 7);
-                    o[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb, o[cb], 0, 0, 0);
+#pragma unroll
+                    for (int rb = 0; rb < kRB; ++rb)
+                        o[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[rb], o[rb][cb], 0, 0, 0);
                 }
             }
 
-            // two transposed V reads per P.V MFMA, eight ahead
+            // two transposed V reads per column block's MFMAs, one group ahead
 #pragma unroll
             for (int i = 0; i < kColBlocks - kVGroup; ++i) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+                __builtin_amdgcn_sched_group_barrier(0x008, kRB, 1);
                 __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
             }
-            __builtin_amdgcn_sched_group_barrier(0x008, kVGroup, 1);
+            __builtin_amdgcn_sched_group_barrier(0x008, kVGroup * kRB, 1);
             if (++t >= ntiles)
                 break;
             next_tile(t);
@@ -741,51 +845,83 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(Args a, int slots, i
             break;
         // Some row of this wave outgrew its reference on tile t: raise every
         // row's reference to its running max, rescale, and redo tile t.
-        mt = fmaxf(mt, __shfl_xor(mt, 16));
-        mt = fmaxf(mt, __shfl_xor(mt, 32));
-        const float m_new = fmaxf(m_ref, mt);
-        const float alpha = (m_ref == -INFINITY) ? 0.f : exp2f(m_ref - m_new);
-        m_ref = m_new;
-        l_run *= alpha;
 #pragma unroll
-        for (int cb = 0; cb < kColBlocks; ++cb)
-            o[cb] *= alpha;
+        for (int rb = 0; rb < kRB; ++rb) {
+            float m = fmaxf(mt[rb], __shfl_xor(mt[rb], 16));
+            m = fmaxf(m, __shfl_xor(m, 32));
+            const float m_new = fmaxf(m_ref[rb], m);
+            const float alpha = (m_ref[rb] == -INFINITY) ? 0.f : exp2f(m_ref[rb] - m_new);
+            m_ref[rb] = m_new;
+            l_run[rb] *= alpha;
+            if constexpr (kRB == 1) {
+#pragma unroll
+                for (int cb = 0; cb < kColBlocks; ++cb)
+                    o[rb][cb] *= alpha;
+            } else {
+                // O fills every accumulation register here, and a plain
+                // multiply makes the compiler move it through memory on every
+                // tile; so each value is scaled in place, one accumulation
+                // register at a time. No MFMA is in flight on O: the MFMA pipe
+                // retires in order and the last Q.K^T result was read before
+                // this point, and the next MFMA that reads O follows a whole
+                // Q.K^T of the redone tile.
+#pragma unroll
+                for (int cb = 0; cb < kColBlocks; ++cb)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        float e = o[rb][cb][i];
+                        float tmp;
+                        asm volatile("v_accvgpr_read_b32 %1, %0\n\t"
+                                     "v_mul_f32 %1, %1, %2\n\t"
+                                     "v_accvgpr_write_b32 %0, %1"
+                                     : "+a"(e), "=&v"(tmp)
+                                     : "v"(alpha));
+                        o[rb][cb][i] = e;
+                    }
+            }
+        }
     }
 
-    // Partial result of this slice, in the register-fragment order.
-    float l_tot = l_run + __shfl_xor(l_run, 16);
-    l_tot += __shfl_xor(l_tot, 32);
-    const size_t pidx = (size_t)grp * max_slices + gslice;
-    // O is stored rounded to bf16 (round to nearest even, relative error at
-    // most 2^-8 per element); the combine scales each slice's O by a factor of
-    // at most 1, so the merged output carries at most that relative error per
-    // slice term. It halves the partial traffic; the running max and sum stay
-    // fp32, so the lse is unaffected. The stores are device-scope: written
-    // through this XCD's L2 (the combine runs on every XCD and reads past
-    // it), so the end of the kernel has no dirty lines to write back. They go
-    // out before the wait for the last prefetch gathers, so that the two
-    // latencies overlap.
-    __bf16* po = (__bf16*)a.part_o + pidx * (size_t)(kRowsPerGroup * kPartRowElems) +
-                 (size_t)wave * (kColBlocks * 64 * 4);
+    // Partial results of this slice, in the register-fragment order.
 #pragma unroll
-    for (int cb = 0; cb < kColBlocks; ++cb) {
-        bf16x4 v;
+    for (int rb = 0; rb < kRB; ++rb) {
+        const int rg = grp * kRB + rb;
+        if (kRB > 1 && rg >= row_groups)
+            break;  // uniform: a last workgroup group with one row group
+        float l_tot = l_run[rb] + __shfl_xor(l_run[rb], 16);
+        l_tot += __shfl_xor(l_tot, 32);
+        const size_t pidx = (size_t)rg * max_slices + gslice;
+        // O is stored rounded to bf16 (round to nearest even, relative error
+        // at most 2^-8 per element); the combine scales each slice's O by a
+        // factor of at most 1, so the merged output carries at most that
+        // relative error per slice term. It halves the partial traffic; the
+        // running max and sum stay fp32, so the lse is unaffected. The stores
+        // are device-scope: written through this XCD's L2 (the combine runs on
+        // every XCD and reads past it), so the end of the kernel has no dirty
+        // lines to write back. They go out before the wait for the last
+        // prefetch gathers, so that the two latencies overlap.
+        __bf16* po = (__bf16*)a.part_o + pidx * (size_t)(kRowsPerGroup * kPartRowElems) +
+                     (size_t)wave * (kColBlocks * 64 * 4);
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            v[i] = (__bf16)o[cb][i];
-        __hip_atomic_store((uint64_t*)(po + (cb * 64 + lane) * 4), __builtin_bit_cast(uint64_t, v),
-                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-    if (lg == 0) {
-        float2* pm = (float2*)a.part_ml + pidx * kRowsPerGroup + wave * 16 + rl;
-        __hip_atomic_store((uint64_t*)pm, __builtin_bit_cast(uint64_t, make_float2(m_ref, l_tot)),
-                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        for (int cb = 0; cb < kColBlocks; ++cb) {
+            bf16x4 v;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                v[i] = (__bf16)o[rb][cb][i];
+            __hip_atomic_store((uint64_t*)(po + (cb * 64 + lane) * 4), __builtin_bit_cast(uint64_t, v),
+                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        if (lg == 0) {
+            float2* pm = (float2*)a.part_ml + pidx * kRowsPerGroup + wave * 16 + rl;
+            __hip_atomic_store((uint64_t*)pm, __builtin_bit_cast(uint64_t, make_float2(m_ref[rb], l_tot)),
+                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
     }
     // The last prefetch gathers write LDS, so they must land before the
-    // workgroup ends. The 32 stores of O above are younger than every
-    // gather and are always issued, and vmcnt retires in order: at most 32
-    // outstanding operations means every gather has landed, without waiting
-    // for the stores.
+    // workgroup ends. The 32 stores of O of the first row block are younger
+    // than every gather and are always issued, and vmcnt retires in order: at
+    // most 32 outstanding operations means every gather has landed, without
+    // waiting for the stores.
     wait_vmcnt<kColBlocks>();
 }
 
@@ -988,8 +1124,15 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(Args a, int si
 hipError_t launch_split(const Plan& p, const Args& a, hipStream_t stream)
 {
     const float scale_log2 = (float)((double)a.scale * 1.4426950408889634);
-    const int per_xcd = xcd_block(p.max_slices * p.row_groups, p.row_groups);
-    hipLaunchKernelGGL(a.prefix_pages ? split_kernel<true> : split_kernel<false>, dim3(8 * per_xcd),
+    const int wg_groups = (p.row_groups + p.rb - 1) / p.rb;
+    const int per_xcd = xcd_block(p.max_slices * wg_groups, wg_groups);
+    // two row blocks per wave only with per-token tables (the plan never
+    // pairs them with the hybrid layout)
+    if (p.rb == 2 && a.prefix_pages)
+        return hipErrorInvalidValue;
+    auto kernel = p.rb == 2 ? split_kernel<false, 2>
+                            : (a.prefix_pages ? split_kernel<true, 1> : split_kernel<false, 1>);
+    hipLaunchKernelGGL(kernel, dim3(8 * per_xcd),
                        dim3(kThreads), 0, stream, a, p.slots, p.single_c, p.max_slices, p.row_groups,
                        scale_log2);
     return hipGetLastError();

@@ -70,6 +70,25 @@ def test_plan_covers_every_key(b, n, h, max_kv, cus):
     assert pairs * p["splits"] >= min(cus, pairs * tiles) // 2
 
 
+@pytest.mark.parametrize("n,h,max_kv,splits", [
+    (64, 64, 131136, 8),    # 64 row groups, 513-tile slices: two row groups per workgroup
+    (64, 17, 131136, 29),   # 17 row groups (9 workgroup groups), 142-tile slices: two
+    (64, 16, 65600, 16),    # 16 row groups but 129-tile slices would be 65: one
+    (16, 8, 65552, 121),    # 2 row groups: one
+])
+def test_two_row_group_plan_rule(n, h, max_kv, splits):
+    """Two 64-row groups share a split workgroup from 16 row groups and 128
+    tiles per slice on: on 256 CUs the slot count then doubles."""
+    p = M.plan_query(M.make_shape(1, n, h, max_kv, 1 << 20), 256)
+    assert p["splits"] == splits, p
+
+
+def test_noalloc_scratch_covers_one_sequence_of_up_to_32768_rows():
+    for h in (64, 128, 512):
+        for kv in (1024, 131136, 1 << 22):
+            assert M.workspace_size(M.make_shape(1, 64, h, kv, 1 << 20)) <= _lib.NOALLOC_SCRATCH_BYTES
+
+
 def _call(shape, ptrs=None, ws_bytes=1 << 30, scale=0.07):
     lib = M.load()
     good = 1 << 20  # a 256-byte-aligned stand-in address; never dereferenced on the host

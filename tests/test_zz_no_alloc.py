@@ -67,8 +67,8 @@ def test_two_calls_second_smaller_batch():
 
 
 def test_oversized_call_is_rejected_and_enqueues_nothing():
-    # 256 sequences of 16 nodes x 8 heads need more partials than the scratch holds
-    B, N, H = 256, 16, 8
+    # 1024 sequences of 16 nodes x 8 heads need more partials than the scratch holds
+    B, N, H = 1024, 16, 8
     shape = M.make_shape(B, N, H, 64, 4096)
     assert M.workspace_size(shape) > _lib.NOALLOC_SCRATCH_BYTES
     q = torch.zeros((B, N, H, 576), dtype=torch.bfloat16, device="cuda")
