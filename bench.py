@@ -138,7 +138,11 @@ class ClockSampler:
             self.proc = None
         return self
 
-    def stop(self):
+    def stop(self, window=None):
+        """Stop sampling; summarise all samples, the samples with the
+        graphics engine busy, and those inside `window` = (t0, t1, lag): the
+        wall-clock span of a sustained load, less its first `lag` seconds (the
+        driver's activity and clock readings trail the load by up to a second)."""
         if self.proc is None:
             return None
         self.proc.terminate()
@@ -170,7 +174,12 @@ class ClockSampler:
             return out
 
         busy = [r for r in recs if (r.get("gfx_activity_pct") or 0) >= 50]
-        return {"period_s": self.period, "all": summary(recs), "gfx_busy": summary(busy) if busy else None}
+        res = {"period_s": self.period, "all": summary(recs), "gfx_busy": summary(busy) if busy else None}
+        if window is not None:
+            t0, t1, lag = window
+            load = [r for r in recs if t0 + lag <= r["t"] <= t1]
+            res["under_load"] = summary(load) if load else None
+        return res
 
 
 def copy_calibration(mib, torch):
@@ -184,6 +193,22 @@ def copy_calibration(mib, torch):
     torch.cuda.synchronize()
     log("copy calibration: 3 x %d MiB read + %d MiB written" % (mib, mib))
     del src, dst
+
+
+def sustain(calls, seconds, torch):
+    """Back-to-back calls for about `seconds` of wall clock (chunks of 200,
+    synchronised), so that a clock sampler sees a sustained load; returns the
+    window (start, end) and the mean wall-clock microseconds per call."""
+    torch.cuda.synchronize()
+    t0 = time.time()
+    n = 0
+    while time.time() - t0 < seconds:
+        for k in range(200):
+            calls[k % len(calls)].run()
+        torch.cuda.synchronize()
+        n += 200
+    t1 = time.time()
+    return t0, t1, (t1 - t0) / n * 1e6
 
 
 def time_calls(calls, steps, warmup, torch):
@@ -278,7 +303,7 @@ def headline(args, torch, M, I):
     plan = M.plan_query(M.make_shape(1, n, h, wls[0].max_kv, wls[0].num_slots),
                         torch.cuda.get_device_properties(0).multi_processor_count)
     per_call = time_each_call(calls, args.steps, torch)
-    return dict(wls=wls, sec=sec, call_bytes=call_bytes, split_avg_ms=avg_ms,
+    return dict(wls=wls, calls=calls, sec=sec, call_bytes=call_bytes, split_avg_ms=avg_ms,
                 split_med_ms=med_ms, split_bytes=kbytes, plan=plan,
                 call_us={"p10": round(pct(per_call, 0.1), 3), "p50": round(pct(per_call, 0.5), 3),
                          "p90": round(pct(per_call, 0.9), 3)})
@@ -322,8 +347,10 @@ def other_configs(args, torch, M, I):
             c = M.prepare_workload(wl, workspace=ws)
             ws = c.workspace
             calls.append(c)
-        for c in calls:
-            c.run()
+        # about 20 ms of untimed calls first: the earliest calls after the
+        # inputs are built run up to 10 % slower
+        for k in range(20):
+            calls[k % len(calls)].run()
         us = time_each_call(calls, args.big_steps, torch)
         sk = time_each_call(calls, args.big_steps, torch, "splitkv")
         seq = wls[0].seq_lens_host()
@@ -340,7 +367,10 @@ def other_configs(args, torch, M, I):
             "peak_tflops": PEAK_BF16_TFLOPS,
             "split_kernel_frac": round(flops / (ksk * 1e-6) / 1e12 / PEAK_BF16_TFLOPS, 4),
             "gbps": round(I.algorithmic_bytes(seq, n, h) / (med * 1e-6) / 1e9, 1),
-            "flops_per_call": flops}
+            "flops_per_call": flops,
+            # SQ_VALU_MFMA_BUSY_CYCLES share of the split kernel in the committed
+            # counter profile of the same kernel source (null if it differs)
+            "split_mfma_busy_pct": (measured_profile() or {}).get("random64-h64-ctx131072_split_mfma_busy_pct")}
         log("random64-h64-ctx131072: %.1f us/call, %.1f TFLOP/s (split kernel %.1f us, %.1f TFLOP/s)"
             % (med, flops / (med * 1e-6) / 1e12, ksk, flops / (ksk * 1e-6) / 1e12))
         del calls, wls, ws
@@ -766,8 +796,9 @@ def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=200,
-                    help="untimed calls first (about 8 ms of work, so that clocks settle)")
+    ap.add_argument("--warmup", type=int, default=25000,
+                    help="untimed calls first (about 1 s of work: the GPU's clocks ramp up from "
+                         "idle over the first second of load)")
     ap.add_argument("--rotate", type=int, default=8, help="independent input sets cycled over")
     ap.add_argument("--sweep", default=SWEEP_CONTEXTS,
                     help="contexts of the 61-layer chain8 sweep ('' to skip)")
@@ -780,6 +811,8 @@ def main() -> int:
                          "kv (Tier-0 defrag and accepted-path commit); '' for none")
     ap.add_argument("--big-steps", type=int, default=20, help="timed calls of the c4 configuration")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--clock-seconds", type=float, default=3.0,
+                    help="seconds of back-to-back headline calls read by the clock sampler")
     ap.add_argument("--no-clocks", action="store_true",
                     help="skip the amdsmi clock/power sampler (e.g. under a profiler)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -822,7 +855,16 @@ def main() -> int:
         % (sec * 1e6, value, hd["split_avg_ms"] * 1e3, hd["split_med_ms"] * 1e3, achieved))
 
     sw = sweep(args, torch, M, I)
-    clocks = sampler.stop() if sampler is not None else None
+    clocks = None
+    if sampler is not None:
+        # the timed work above takes about a second; the sampler needs a
+        # sustained load of a few seconds to read the clocks under it
+        t0, t1, us_sus = sustain(hd["calls"], args.clock_seconds, torch)
+        clocks = sampler.stop(window=(t0, t1, 1.0))
+        if clocks is not None:
+            clocks["load"] = {"workload": "binary16-ctx65536 calls back to back",
+                              "seconds": round(t1 - t0, 2), "us_per_call": round(us_sus, 2)}
+        log("sustained headline calls for %.1f s: %.2f us/call" % (t1 - t0, us_sus))
     oc = other_configs(args, torch, M, I)
     cpu = None if args.no_cpu_baseline else cpu_baseline(hd["wls"], hd["call_bytes"], I)
 
