@@ -376,73 +376,55 @@ def other_configs(args, torch, M, I):
         del calls, wls, ws
         torch.cuda.empty_cache()
     if "c5" in names:
-        res = {}
-        outs = {}
+        # The layouts are timed in alternating rounds (each one freshly built
+        # layout runs slower for its first calls, and back-to-back phases drift
+        # by 1-2 us on their own): the scattered per-token table, the same rows
+        # relaid in runs of 64 slots, the hybrid layout (prefixes in pages of 64
+        # slots, tree rows scattered) through mla_tree_verify_paged, and that
+        # layout's pool through its expanded per-token table.
         base = I.config_workload(5, device="cuda", layout="scattered")
-        for layout in ("scattered", "runs64"):
-            log("building batch8-loguniform (%s)" % layout)
-            # identical logical values in both layouts: the runs-of-64 pool
-            # holds the scattered pool's rows at the new table's slots
-            wl = base if layout == "scattered" else I.relayout(
-                base, I.seed_for(5, 0, I.F_TABLE) + 1, "runs64")
-            c = M.prepare_workload(wl)
-            c.run()
-            torch.cuda.synchronize()
-            outs[layout] = (c.out.clone(), c.lse.clone())
-            for _ in range(C5_WARMUP):  # a freshly built layout runs slower for its first calls
-                c.run()
-            us = time_each_call([c], args.steps, torch)
-            seq = wl.seq_lens_host()
-            b = I.algorithmic_bytes(seq, wl.num_nodes, wl.num_heads)
-            med = pct(us, 0.5)
-            res[layout] = {"us_per_call": {"p10": round(pct(us, 0.1), 2), "p50": round(med, 2),
-                                           "p90": round(pct(us, 0.9), 2)},
-                           "gbps": round(b / (med * 1e-6) / 1e9, 1),
-                           "pct_of_peak": round(100 * b / (med * 1e-6) / 1e9 / PEAK_GBPS, 2),
-                           "bytes_per_call": b, "seq_lens": [int(x) for x in seq]}
-            log("batch8-loguniform %s: %.2f us/call, %.0f GB/s" % (layout, med, b / (med * 1e-6) / 1e9))
-            del c, wl
-            torch.cuda.empty_cache()
-        # hybrid paging: prefixes in whole pages of 64 slots, tree rows at
-        # scattered slots, addressed by page list + tree slot list
-        log("building batch8-loguniform (hybrid pages of 64)")
+        runs = I.relayout(base, I.seed_for(5, 0, I.F_TABLE) + 1, "runs64")
         hl = I.hybrid_layout(base, 64, seed=64)
         w = hl.workload
-        out_t = torch.empty((w.batch, w.num_nodes, w.num_heads, 512), dtype=torch.bfloat16, device="cuda")
-        lse_t = torch.empty((w.batch, w.num_nodes, w.num_heads), dtype=torch.float32, device="cuda")
-        ws_t = torch.zeros(M.workspace_size(M.make_shape(w.batch, w.num_nodes, w.num_heads, w.max_kv,
-                                                         w.num_slots)), dtype=torch.uint8, device="cuda")
-
-        class _Paged:
-            def run(self):
-                M.mla_tree_verify_paged(w.q, w.kv_pool, hl.prefix_pages, hl.tree_slots, w.seq_lens,
-                                        w.tree_mask, w.scale, 64, w.max_kv, out=out_t, lse=lse_t,
-                                        workspace=ws_t)
-        _Paged().run()
+        log("building batch8-loguniform (scattered, runs64, hybrid pages of 64)")
+        calls = {"scattered": M.prepare_workload(base), "runs64": M.prepare_workload(runs),
+                 "paged64": M.PreparedPagedCall(w.q, w.kv_pool, hl.prefix_pages, hl.tree_slots, w.seq_lens,
+                                                w.tree_mask, w.scale, 64, w.max_kv),
+                 "paged64_pool_per_token": M.prepare_workload(w)}
         torch.cuda.synchronize()
-        outs["paged64"] = (out_t.clone(), lse_t.clone())
-        for _ in range(C5_WARMUP):
-            _Paged().run()
-        us = time_each_call([_Paged()], args.steps, torch)
-        seq = w.seq_lens_host()
-        b = I.algorithmic_bytes(seq, w.num_nodes, w.num_heads)
-        med = pct(us, 0.5)
-        res["paged64"] = {"us_per_call": {"p10": round(pct(us, 0.1), 2), "p50": round(med, 2),
-                                          "p90": round(pct(us, 0.9), 2)},
-                          "gbps": round(b / (med * 1e-6) / 1e9, 1),
-                          "pct_of_peak": round(100 * b / (med * 1e-6) / 1e9 / PEAK_GBPS, 2),
-                          "bytes_per_call": b, "page_size": 64,
-                          "page_list_entries": int(hl.prefix_pages.numel())}
-        log("batch8-loguniform paged64: %.2f us/call, %.0f GB/s" % (med, b / (med * 1e-6) / 1e9))
-        del hl, w, out_t, lse_t, ws_t, base
-        torch.cuda.empty_cache()
+        outs = {k: (c.out.clone(), c.lse.clone()) for k, c in calls.items()}
+        for c in calls.values():
+            for _ in range(C5_WARMUP):
+                c.run()
+        us = {k: [] for k in calls}
+        rounds = 5
+        for _ in range(rounds):
+            for k, c in calls.items():
+                us[k] += time_each_call([c], max(1, args.steps // rounds), torch)
+        seq = base.seq_lens_host()
+        b = I.algorithmic_bytes(seq, base.num_nodes, base.num_heads)
+        res = {}
+        for k in calls:
+            v = sorted(us[k])
+            med = pct(v, 0.5)
+            res[k] = {"us_per_call": {"p10": round(pct(v, 0.1), 2), "p50": round(med, 2),
+                                      "p90": round(pct(v, 0.9), 2)},
+                      "gbps": round(b / (med * 1e-6) / 1e9, 1),
+                      "pct_of_peak": round(100 * b / (med * 1e-6) / 1e9 / PEAK_GBPS, 2),
+                      "bytes_per_call": b}
+            log("batch8-loguniform %s: %.2f us/call, %.0f GB/s" % (k, med, b / (med * 1e-6) / 1e9))
+        res["seq_lens"] = [int(x) for x in seq]
+        res["paged64"]["page_size"] = 64
+        res["paged64"]["page_list_entries"] = int(hl.prefix_pages.numel())
+        res["rounds"] = rounds
 
         def same(x, y):
             return bool(torch.equal(x[0].view(torch.int16), y[0].view(torch.int16))
                         and torch.equal(x[1].view(torch.int32), y[1].view(torch.int32)))
-        res["bitwise_equal"] = same(outs["scattered"], outs["runs64"]) and same(outs["scattered"],
-                                                                              outs["paged64"])
+        res["bitwise_equal"] = all(same(outs["scattered"], o) for o in outs.values())
         out["batch8-loguniform"] = res
+        del calls, base, runs, hl, w
+        torch.cuda.empty_cache()
     if "mask" in names:
         # the tree-mask build before the verify step (parent array -> bitmask)
         import numpy as np

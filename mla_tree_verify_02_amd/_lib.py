@@ -466,6 +466,48 @@ class PreparedCall:
             raise MtvError(rc, status_string(rc))
 
 
+class PreparedPagedCall:
+    """PreparedCall for the hybrid layout (mla_tree_verify_paged): one
+    validating call through the full binding, then ``run()`` only marshals the
+    held pointers."""
+
+    def __init__(self, q, kv_pool, prefix_pages, tree_slots, seq_lens, tree_mask, scale, page_size,
+                 max_kv, workspace=None):
+        B, N, H, _ = q.shape
+        dev = q.device
+        self.out = torch.empty((B, N, H, 512), dtype=torch.bfloat16, device=dev)
+        self.lse = torch.empty((B, N, H), dtype=torch.float32, device=dev)
+        self.shape = make_shape(B, N, H, max_kv, kv_pool.shape[0])
+        need = workspace_size(self.shape)
+        if need == 0:
+            raise MtvError(-2, status_string(-2))
+        if workspace is None or workspace.numel() * workspace.element_size() < need:
+            workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+        self.workspace = workspace
+        self.inputs = (q, kv_pool, prefix_pages, tree_slots, seq_lens, tree_mask)
+        self.scale = float(scale)
+        self.page_size = int(page_size)
+        self.max_pages = int(prefix_pages.shape[1])
+        self.device = dev
+        mla_tree_verify_paged(q, kv_pool, prefix_pages, tree_slots, seq_lens, tree_mask, scale,
+                              page_size, max_kv, out=self.out, lse=self.lse, workspace=self.workspace)
+        self._lib = load()
+        self._p = [ctypes.c_void_p(t.data_ptr()) for t in self.inputs]
+        self._out = ctypes.c_void_p(self.out.data_ptr())
+        self._lse = ctypes.c_void_p(self.lse.data_ptr())
+        self._ws = ctypes.c_void_p(self.workspace.data_ptr())
+        self._wsb = ctypes.c_size_t(self.workspace.numel() * self.workspace.element_size())
+
+    def run(self):
+        q, kv, pp, ts, sl, tm = self._p
+        rc = self._lib.mla_tree_verify_paged(ctypes.byref(self.shape), self.page_size, self.max_pages, q,
+                                             kv, pp, ts, sl, tm, ctypes.c_float(self.scale), self._out,
+                                             self._lse, self._ws, self._wsb,
+                                             ctypes.c_void_p(torch.cuda.current_stream(self.device).cuda_stream))
+        if rc != MTV_OK:
+            raise MtvError(rc, status_string(rc))
+
+
 def prepare_workload(wl, workspace=None) -> PreparedCall:
     return PreparedCall(wl.q, wl.kv_pool, wl.page_table, wl.seq_lens, wl.tree_mask, wl.scale,
                         workspace=workspace)

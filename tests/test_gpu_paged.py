@@ -209,3 +209,21 @@ def test_long_slices_restage_paged_window(oracle_mod):
     out, lse = check_bitwise(w, hl.prefix_pages, hl.tree_slots, 64, table)
     rows = np.unique(np.r_[0, 2047, np.random.default_rng(3).choice(2048, 40, replace=False)])
     check_vs_oracle(oracle_mod, w, table, out, lse, rows=rows, label="paged long slices")
+
+
+def test_prepared_paged_call_matches_the_call():
+    """PreparedPagedCall.run (pointers marshalled once) gives the bits of
+    mla_tree_verify_paged, on every repeat."""
+    wl = I.config_workload(5, device="cuda")
+    hl = I.hybrid_layout(wl, 64, seed=64)
+    w = hl.workload
+    ref_o, ref_l = run_paged(w, hl.prefix_pages, hl.tree_slots, 64)
+    call = M.PreparedPagedCall(w.q, w.kv_pool, hl.prefix_pages, hl.tree_slots, w.seq_lens, w.tree_mask,
+                               w.scale, 64, w.max_kv)
+    for _ in range(3):
+        call.out.zero_()
+        call.lse.zero_()
+        call.run()
+        torch.cuda.synchronize()
+        assert torch.equal(call.out.view(torch.int16), ref_o.view(torch.int16))
+        assert torch.equal(call.lse.view(torch.int32), ref_l.view(torch.int32))
