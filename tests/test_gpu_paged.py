@@ -227,3 +227,19 @@ def test_prepared_paged_call_matches_the_call():
         torch.cuda.synchronize()
         assert torch.equal(call.out.view(torch.int16), ref_o.view(torch.int16))
         assert torch.equal(call.lse.view(torch.int32), ref_l.view(torch.int32))
+
+
+def test_many_rows_long_slices_keep_one_row_group(oracle_mod):
+    """64 nodes x 64 heads at 131072 keys under hybrid paging: the per-token
+    plan runs two row groups per workgroup here, the hybrid call keeps one
+    (its own slicing), and the one workspace size serves both."""
+    wl = I.config_workload(4, device="cuda", q_gain=4.0)
+    hl = I.hybrid_layout(wl, 64, seed=4)
+    w = hl.workload
+    per_token_splits = M.plan_query(M.make_shape(1, 64, 64, w.max_kv, w.num_slots),
+                                    torch.cuda.get_device_properties(0).multi_processor_count)["splits"]
+    out, lse = run_paged(w, hl.prefix_pages, hl.tree_slots, 64)
+    table = oracle_expand(w, hl.prefix_pages, hl.tree_slots, 64)
+    rng = np.random.default_rng(41)
+    rows = np.unique(np.r_[0, 4095, [g * 64 + rng.integers(64) for g in range(64)]])
+    check_vs_oracle(oracle_mod, w, table, out, lse, rows=rows, label=f"paged64 h64 (per-token plan {per_token_splits} slices)")
