@@ -1,7 +1,8 @@
 // gfx950 kernels for absorbed-MLA tree-verify attention over a page_size=1 pool.
 //
 // split_kernel: one workgroup = one key slice of one sequence x up to 64 query
-//   rows (4 waves x 16 rows). Per slice it stages the page indices in LDS (by
+//   rows (4 waves x 16 rows), or x 128 (4 waves x 32 rows) for calls with many
+//   rows and long slices. Per slice it stages the page indices in LDS (by
 //   direct global->LDS word loads), then streams 32-key tiles through a
 //   3-buffer LDS ring filled by direct
 //   global->LDS 16-byte loads (each 1152-byte latent row is nine full 128-byte
