@@ -127,3 +127,44 @@ def test_split_then_combine_equals_the_call(cid):
     torch.cuda.synchronize()
     assert np.array_equal(call.out.view(torch.int16).cpu().numpy().view(np.uint16), ref[0])
     assert np.array_equal(call.lse.cpu().numpy().view(np.uint32), ref[1].view(np.uint32))
+
+
+def test_batch_above_64_sequences(oracle_mod):
+    """80 sequences of 64 x 16 rows (4,200-6,000 keys each, one slice of at
+    least 131 tiles per sequence): more sequences than a wave has lanes, so the
+    block-wide slicing path feeds the two-row-group form."""
+    rng = np.random.default_rng(124)
+    pre = [int(x) for x in rng.integers(4200, 6000, size=80)]
+    wl = I.make_workload(batch=80, num_nodes=64, num_heads=16, prefix_lens=pre, num_slots=524288,
+                         tree="random", max_depth=8, config_id=124, device="cuda", q_gain=4.0)
+    assert_two_row_blocks(wl)
+    R = 64 * 16
+    rows = np.unique(np.r_[0, 80 * R - 1, [b * R + g * 64 + rng.integers(64)
+                                             for b in (0, 1, 37, 63, 64, 79) for g in range(16)]])
+    compare(wl, oracle_mod, rows=rows, label="two row blocks, batch 80")
+
+
+def test_graph_capture_replays_match_eager():
+    """A captured two-row-group call (64 x 64 heads at 131072 keys): every
+    replay, with eager work between replays, gives the eager call's bits."""
+    wl = I.config_workload(4, device="cuda")
+    ref = run_gpu(wl)
+    call = M.prepare_workload(wl)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        call.run()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call.run()
+    other = I.config_workload(1, device="cuda")
+    for _ in range(3):
+        call.out.zero_()
+        call.lse.zero_()
+        g.replay()
+        M.verify_workload(other)  # eager work between replays
+        torch.cuda.synchronize()
+        assert np.array_equal(call.out.view(torch.int16).cpu().numpy().view(np.uint16), ref[0])
+        assert np.array_equal(call.lse.cpu().numpy().view(np.uint32), ref[1].view(np.uint32))
