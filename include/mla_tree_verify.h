@@ -155,7 +155,10 @@ int mla_tree_verify(const mtv_shape* shape,
  *   p <  t0:  prefix_pages[b][p / page_size] * page_size + p % page_size
  *   p >= t0:  tree_slots[b][p - t0]           (tree node p - t0)
  * and everything else is exactly mla_tree_verify: the result equals an
- * mla_tree_verify call whose page_table holds those slots, bit for bit.
+ * mla_tree_verify call whose page_table holds those slots, bit for bit, when
+ * that call also runs one 64-row group per split workgroup. This call always
+ * does; mla_tree_verify runs two on many rows over long slices (see
+ * mtv_plan_query), and then its slices, and so its rounding, differ.
  *   page_size    in [1, MTV_MAX_KV] (64 is the pages' figure)
  *   max_pages    row length of prefix_pages, >= ceil((max_kv - N) / page_size)
  *                for every position to have a page; a page number beyond the
@@ -380,9 +383,9 @@ const char* mtv_status_string(int status);
  * and 64-row groups per sequence (*row_groups). Batches of other lengths are
  * sliced on the device from seq_lens with the same rule (slices of one size
  * for the whole batch, sized from its total key count). This is the plan of
- * the per-token-table calls: from 16 row groups and 128 tiles (4096 keys) per
- * slice on, two row groups share a split workgroup and the slots per row group
- * double; mla_tree_verify_paged always runs one row group per workgroup, so
+ * the per-token-table calls: from 16 row groups and 48 tiles (1536 keys) per
+ * slice, or from 8 row groups and 64 tiles, two row groups share a split
+ * workgroup and the slots per row group double; mla_tree_verify_paged always runs one row group per workgroup, so
  * its slicing can differ. Host-only arithmetic.
  * Returns MTV_OK, MTV_ERR_NULL or MTV_ERR_SHAPE.
  */

@@ -95,18 +95,20 @@ mtv::Plan make_plan_rb(const mtv_shape& s, int cus, int rb)
 // Many rows over long slices make the call MFMA-bound: then two row groups
 // share each split workgroup (two 16-row blocks per wave), which halves the
 // LDS operand reads per MFMA and the tile gathers per row. That form costs
-// about 34 us more per call (its rare-rescale path keeps spill space, set up
-// by every wave) and saves about 0.37 us per tile of a slice (measured on
-// 64 x 64 heads at 131072 keys and on 16 and 32 row groups at 32768-65536
-// keys), so it is taken only from 16 row groups and 128 tiles per slice.
-// Per-token tables only: the hybrid layout's index staging leaves that form
-// no registers to spare.
+// about 12-17 us more per call (two blocks of Q to load, tile 0's Q.K^T ahead
+// of the loop, twice the partials to store and, with the slots per row group
+// doubled, to combine) and saves about 0.3-0.45 us per tile of a slice.
+// Measured on 16, 32 and 64 row groups at 8192-65536 keys, it breaks even
+// near 40 tiles per slice; on 8 row groups, whose slices are shared by fewer
+// workgroups, near 50. So it is taken from 16 row groups and 48 tiles per
+// slice, or from 8 row groups and 64. Per-token tables only: the hybrid
+// layout's index staging leaves that form no registers to spare.
 mtv::Plan make_plan(const mtv_shape& s, int cus, bool paged)
 {
     const int row_groups = (s.num_nodes * s.num_heads + mtv::kRowsPerGroup - 1) / mtv::kRowsPerGroup;
     if (!paged && row_groups >= mtv::kRB2MinRowGroups) {
         const mtv::Plan p2 = make_plan_rb(s, cus, 2);
-        if (p2.single_c >= mtv::kRB2MinTiles)
+        if (p2.single_c >= mtv::kRB2MinTiles(row_groups))
             return p2;
     }
     return make_plan_rb(s, cus, 1);

@@ -14,8 +14,10 @@ constexpr int kDv = 512;           // value width (the latent)
 constexpr int kRowBytes = kDqk * 2;
 constexpr int kTileKeys = 32;      // keys per LDS tile
 constexpr int kRowsPerGroup = 64;  // query rows per row group (4 waves x 16)
-constexpr int kRB2MinRowGroups = 16;  // two row groups per split workgroup from this many
-constexpr int kRB2MinTiles = 128;     // ... and from this many tiles per slice
+// Two row groups per split workgroup from 16 row groups and 48 tiles per
+// slice, or from 8 row groups and 64 tiles per slice.
+constexpr int kRB2MinRowGroups = 8;
+constexpr int kRB2MinTiles(int row_groups) { return row_groups >= 16 ? 48 : 64; }
 
 // How one call is cut into workgroups. Depends only on host values.
 struct Plan {

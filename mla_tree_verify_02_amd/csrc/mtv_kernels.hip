@@ -35,6 +35,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 #define LDS_AS __attribute__((address_space(3)))
+#define GLOBAL_AS __attribute__((address_space(1)))
 
 constexpr int kThreads = 256;
 constexpr int kWaves = 4;
@@ -686,6 +687,13 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(Args a, int slots, i
     while (true) {
         float x[kRB][8];
         float mt[kRB];
+        // The two-row-block form reloads part of O from scratch here (on entry
+        // and after a raise). Waiting for those loads before the tile loop
+        // keeps the compiler's own waits for them out of the loop body: there
+        // they would run on every tile and, since vector-memory operations
+        // retire in order, also drain the row gathers in flight.
+        if constexpr (kRB > 1)
+            wait_vmcnt<0>();
         for (;;) {
             opaque_plan();
             const char LDS_AS* buf = (const char LDS_AS*)s_kv + (t % kStages) * kTileBytes;
@@ -838,8 +846,15 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(Args a, int slots, i
                 __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
             }
             __builtin_amdgcn_sched_group_barrier(0x008, kVGroup * kRB, 1);
-            if (++t >= ntiles)
-                break;
+            if (++t >= ntiles) {
+                // The two-row-block form leaves straight for the stores: a
+                // shared exit with the raise path below would run that path's
+                // spill code at the end of every slice.
+                if constexpr (kRB > 1)
+                    goto slice_done;
+                else
+                    break;
+            }
             next_tile(t);
         }
         if (t >= ntiles)
@@ -883,47 +898,91 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(Args a, int slots, i
         }
     }
 
+slice_done:
     // Partial results of this slice, in the register-fragment order.
+    // O is stored rounded to bf16 (round to nearest even, relative error at
+    // most 2^-8 per element); the combine scales each slice's O by a factor of
+    // at most 1, so the merged output carries at most that relative error per
+    // slice term. It halves the partial traffic; the running max and sum stay
+    // fp32, so the lse is unaffected. The stores are device-scope: written
+    // through this XCD's L2 (the combine runs on every XCD and reads past it),
+    // so the end of the kernel has no dirty lines to write back. They go out
+    // before the wait for the last prefetch gathers, so that the two latencies
+    // overlap.
+    if constexpr (kRB == 1) {
 #pragma unroll
-    for (int rb = 0; rb < kRB; ++rb) {
-        const int rg = grp * kRB + rb;
-        if (kRB > 1 && rg >= row_groups)
-            break;  // uniform: a last workgroup group with one row group
-        float l_tot = l_run[rb] + __shfl_xor(l_run[rb], 16);
-        l_tot += __shfl_xor(l_tot, 32);
-        const size_t pidx = (size_t)rg * max_slices + gslice;
-        // O is stored rounded to bf16 (round to nearest even, relative error
-        // at most 2^-8 per element); the combine scales each slice's O by a
-        // factor of at most 1, so the merged output carries at most that
-        // relative error per slice term. It halves the partial traffic; the
-        // running max and sum stay fp32, so the lse is unaffected. The stores
-        // are device-scope: written through this XCD's L2 (the combine runs on
-        // every XCD and reads past it), so the end of the kernel has no dirty
-        // lines to write back. They go out before the wait for the last
-        // prefetch gathers, so that the two latencies overlap.
-        __bf16* po = (__bf16*)a.part_o + pidx * (size_t)(kRowsPerGroup * kPartRowElems) +
-                     (size_t)wave * (kColBlocks * 64 * 4);
+        for (int rb = 0; rb < kRB; ++rb) {
+            const int rg = grp * kRB + rb;
+            float l_tot = l_run[rb] + __shfl_xor(l_run[rb], 16);
+            l_tot += __shfl_xor(l_tot, 32);
+            const size_t pidx = (size_t)rg * max_slices + gslice;
+            __bf16* po = (__bf16*)a.part_o + pidx * (size_t)(kRowsPerGroup * kPartRowElems) +
+                         (size_t)wave * (kColBlocks * 64 * 4);
 #pragma unroll
-        for (int cb = 0; cb < kColBlocks; ++cb) {
-            bf16x4 v;
+            for (int cb = 0; cb < kColBlocks; ++cb) {
+                bf16x4 v;
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                v[i] = (__bf16)o[rb][cb][i];
-            __hip_atomic_store((uint64_t*)(po + (cb * 64 + lane) * 4), __builtin_bit_cast(uint64_t, v),
-                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                for (int i = 0; i < 4; ++i)
+                    v[i] = (__bf16)o[rb][cb][i];
+                __hip_atomic_store((uint64_t*)(po + (cb * 64 + lane) * 4), __builtin_bit_cast(uint64_t, v),
+                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+            if (lg == 0) {
+                float2* pm = (float2*)a.part_ml + pidx * kRowsPerGroup + wave * 16 + rl;
+                __hip_atomic_store((uint64_t*)pm, __builtin_bit_cast(uint64_t, make_float2(m_ref[rb], l_tot)),
+                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
         }
-        if (lg == 0) {
-            float2* pm = (float2*)a.part_ml + pidx * kRowsPerGroup + wave * 16 + rl;
-            __hip_atomic_store((uint64_t*)pm, __builtin_bit_cast(uint64_t, make_float2(m_ref[rb], l_tot)),
-                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        // The last prefetch gathers write LDS, so they must land before the
+        // workgroup ends. The 32 stores of O are younger than every gather,
+        // and vmcnt retires in order: at most 32 outstanding operations means
+        // every gather has landed, without waiting for the stores.
+        wait_vmcnt<kColBlocks>();
+    } else {
+        // Every address and (max, sum) pair is formed first and passed through
+        // an empty asm, so that whatever the compiler reloads from scratch for
+        // them lands before the first store: a reload between stores makes it
+        // wait for every store issued before.
+        const int g0 = __builtin_amdgcn_readfirstlane(grp * kRB);  // uniform
+        uint64_t ml[kRB], pm[kRB], po[kRB];
+#pragma unroll
+        for (int rb = 0; rb < kRB; ++rb) {
+            float l_tot = l_run[rb] + __shfl_xor(l_run[rb], 16);
+            l_tot += __shfl_xor(l_tot, 32);
+            const size_t pidx = (size_t)(g0 + rb) * max_slices + gslice;
+            ml[rb] = __builtin_bit_cast(uint64_t, make_float2(m_ref[rb], l_tot));
+            pm[rb] = (uint64_t)((float2*)a.part_ml + pidx * kRowsPerGroup + wave * 16 + rl);
+            po[rb] = (uint64_t)((__bf16*)a.part_o + pidx * (size_t)(kRowsPerGroup * kPartRowElems) +
+                                (size_t)wave * (kColBlocks * 64 * 4) + lane * 4);
         }
+        static_assert(kRB == 2, "the asm below names two row blocks");
+        asm volatile("" : "+v"(ml[0]), "+v"(ml[1]), "+v"(pm[0]), "+v"(pm[1]), "+v"(po[0]), "+v"(po[1]));
+#pragma unroll
+        for (int rb = 0; rb < kRB; ++rb)
+            if (g0 + rb < row_groups && lg == 0)  // a last workgroup group may hold one row group
+                __hip_atomic_store((uint64_t GLOBAL_AS*)pm[rb], ml[rb], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+        for (int rb = 0; rb < kRB; ++rb) {
+            if (g0 + rb >= row_groups)
+                break;  // uniform
+#pragma unroll
+            for (int cb = 0; cb < kColBlocks; ++cb) {
+                bf16x4 v;
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    v[i] = (__bf16)o[rb][cb][i];
+                __hip_atomic_store((uint64_t GLOBAL_AS*)po[rb] + cb * 64, __builtin_bit_cast(uint64_t, v),
+                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+        }
+        // As for one row block, the 32 stores of O of the first row block are
+        // younger than every gather; with a second one 64 are, and 63 (the
+        // counter's limit) leaves the first block's stores in flight too.
+        if (g0 + kRB - 1 < row_groups)
+            wait_vmcnt<63>();
+        else
+            wait_vmcnt<kColBlocks>();
     }
-    // The last prefetch gathers write LDS, so they must land before the
-    // workgroup ends. The 32 stores of O of the first row block are younger
-    // than every gather and are always issued, and vmcnt retires in order: at
-    // most 32 outstanding operations means every gather has landed, without
-    // waiting for the stores.
-    wait_vmcnt<kColBlocks>();
 }
 
 // Merge of one (sequence b, 16-row block rb, group xblk of column units) by

@@ -73,12 +73,20 @@ def test_plan_covers_every_key(b, n, h, max_kv, cus):
 @pytest.mark.parametrize("n,h,max_kv,splits", [
     (64, 64, 131136, 8),    # 64 row groups, 513-tile slices: two row groups per workgroup
     (64, 17, 131136, 29),   # 17 row groups (9 workgroup groups), 142-tile slices: two
-    (64, 16, 65600, 16),    # 16 row groups but 129-tile slices would be 65: one
+    (64, 16, 65600, 32),    # 16 row groups, 65-tile slices: two
+    (64, 16, 49216, 32),    # 49-tile slices: two
+    (64, 16, 40992, 16),    # two would give 41-tile slices: one (81-tile slices)
+    (64, 16, 32800, 16),    # two would give 33-tile slices: one
+    (64, 64, 8256, 4),      # two would give 33-tile slices: one
+    (64, 8, 131136, 64),    # 8 row groups, 65-tile slices: two
+    (64, 8, 98368, 32),     # 8 row groups: two would give 49-tile slices, one
+    (64, 7, 131136, 37),    # 7 row groups: one
     (16, 8, 65552, 121),    # 2 row groups: one
 ])
 def test_two_row_group_plan_rule(n, h, max_kv, splits):
-    """Two 64-row groups share a split workgroup from 16 row groups and 128
-    tiles per slice on: on 256 CUs the slot count then doubles."""
+    """Two 64-row groups share a split workgroup from 16 row groups and 48
+    tiles per slice, or from 8 row groups and 64 tiles: on 256 CUs the slot
+    count then doubles."""
     p = M.plan_query(M.make_shape(1, n, h, max_kv, 1 << 20), 256)
     assert p["splits"] == splits, p
 

@@ -196,18 +196,20 @@ def test_page_size_not_a_power_of_two(oracle_mod, page_size):
 
 
 def test_long_slices_restage_paged_window(oracle_mod):
-    """2048 rows over ~40k keys leave slices of more than one 4096-position
-    window, so the hybrid layout's index staging runs again inside the tile
-    loop; bit for bit equal to the per-token call on the expanded table."""
-    wl = I.make_workload(batch=1, num_nodes=64, num_heads=32, prefix_lens=[40000], num_slots=65536,
+    """7 row groups (64 nodes x 7 heads) over 160k keys leave slices of more
+    than one 4096-position window, so the hybrid layout's index staging runs
+    again inside the tile loop; bit for bit equal to the per-token call on the
+    expanded table, which runs the same one-row-group plan here."""
+    wl = I.make_workload(batch=1, num_nodes=64, num_heads=7, prefix_lens=[160000], num_slots=262144,
                          tree="random", max_depth=8, config_id=107, device="cuda", q_gain=4.0)
-    plan = M.plan_query(M.make_shape(1, 64, 32, wl.max_kv, wl.num_slots), 256)
-    assert plan["chunk"] > 4096, plan
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    plan = M.plan_query(M.make_shape(1, 64, 7, wl.max_kv, wl.num_slots), cus)
+    assert plan["row_groups"] == 7 and plan["chunk"] > 4096, plan
     hl = I.hybrid_layout(wl, 64, seed=5)
     w = hl.workload
     table = oracle_expand(w, hl.prefix_pages, hl.tree_slots, 64)
     out, lse = check_bitwise(w, hl.prefix_pages, hl.tree_slots, 64, table)
-    rows = np.unique(np.r_[0, 2047, np.random.default_rng(3).choice(2048, 40, replace=False)])
+    rows = np.unique(np.r_[0, 447, np.random.default_rng(3).choice(448, 40, replace=False)])
     check_vs_oracle(oracle_mod, w, table, out, lse, rows=rows, label="paged long slices")
 
 

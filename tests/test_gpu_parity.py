@@ -268,13 +268,17 @@ def test_batch8_both_layouts(oracle_mod, q_gain):
 
 
 def test_long_slices_restage_index_window(oracle_mod):
-    """Many row groups leave few, long slices: with 2048 rows over ~40k keys a
-    slice spans more than one 128-tile window of staged page indices, so the
-    kernel restages indices inside its tile loop."""
-    wl = I.make_workload(batch=1, num_nodes=64, num_heads=32, prefix_lens=[40000], num_slots=65536,
+    """Several row groups leave few, long slices: with 7 row groups (64 nodes x
+    7 heads, one row group per workgroup) over 160k keys a slice spans more
+    than one 128-tile window of staged page indices, so the kernel restages
+    indices inside its tile loop. (From 8 row groups on, slices that long run
+    two row groups per workgroup; their restage is covered by the 64 x 64-head
+    tests.)"""
+    wl = I.make_workload(batch=1, num_nodes=64, num_heads=7, prefix_lens=[160000], num_slots=262144,
                          tree="random", max_depth=8, config_id=107, device="cuda", q_gain=4.0)
-    plan = M.plan_query(M.make_shape(1, 64, 32, wl.max_kv, wl.num_slots), 256)
-    assert plan["chunk"] > 128 * 32, plan
+    plan = M.plan_query(M.make_shape(1, 64, 7, wl.max_kv, wl.num_slots),
+                        torch.cuda.get_device_properties(0).multi_processor_count)
+    assert plan["row_groups"] == 7 and plan["chunk"] > 128 * 32, plan
     compare(wl, oracle_mod, rows=sample_rows(wl, 64, seed=7), label="long slices")
 
 

@@ -1,7 +1,8 @@
 """GPU parity of the split kernel's two-row-block form.
 
 Calls with at least 16 row groups of 64 query rows whose slices hold at least
-128 tiles run two row groups per workgroup (two 16-row blocks per wave). The
+48 tiles, or at least 8 row groups with slices of at least 64 tiles, run two
+row groups per workgroup (two 16-row blocks per wave). The
 plan is recognised by its slice count; tolerances and the comparison are those
 of test_gpu_parity (out 2e-2 abs + rel, lse 1e-3 abs + rel, in fp32).
 """
@@ -44,7 +45,7 @@ def assert_two_row_blocks(wl):
     rows = wl.num_nodes * wl.num_heads
     plan = M.plan_query(M.make_shape(wl.batch, wl.num_nodes, wl.num_heads, wl.max_kv, wl.num_slots), cus())
     splits, c = slicing(wl.batch, rows, wl.max_kv, 2)
-    assert rows >= 16 * 64 and c >= 128, (rows, c)
+    assert (rows >= 16 * 64 and c >= 48) or (rows >= 8 * 64 and c >= 64), (rows, c)
     assert plan["splits"] == splits and plan["chunk"] == 32 * c, (plan, splits, c)
 
 
@@ -127,6 +128,18 @@ def test_split_then_combine_equals_the_call(cid):
     torch.cuda.synchronize()
     assert np.array_equal(call.out.view(torch.int16).cpu().numpy().view(np.uint16), ref[0])
     assert np.array_equal(call.lse.cpu().numpy().view(np.uint32), ref[1].view(np.uint32))
+
+
+@pytest.mark.parametrize("heads,keys", [(16, 49152), (16, 65536), (8, 131072)])
+def test_slices_near_the_threshold(oracle_mod, heads, keys):
+    """64 nodes x 16 heads at 49,152 and 65,536 keys (49- and 65-tile slices)
+    and 64 x 8 at 131,072 (65-tile slices): the shortest slices the
+    two-row-group form takes, at gain 4."""
+    wl = I.make_workload(batch=1, num_nodes=64, num_heads=heads, prefix_lens=[keys], num_slots=262144,
+                         tree="random", max_depth=8, config_id=125, device="cuda", q_gain=4.0)
+    assert_two_row_blocks(wl)
+    compare(wl, oracle_mod, rows=rows_of_every_group(wl, 1, seed=125),
+            label=f"two row blocks, 64x{heads} at {keys} keys")
 
 
 def test_batch_above_64_sequences(oracle_mod):
