@@ -411,14 +411,62 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(Args a, int slots, i
     const int32_t* pt = a.page_table + (int64_t)b * a.max_kv;
     const int maxslot = (int)(a.num_slots - 1);
     const int nwin = (ntiles + kWinTiles - 1) / kWinTiles;
+    // Hybrid layout: a prefix position p takes page p / page_size of its row
+    // (a page number past the row reads the last entry) plus p % page_size; a
+    // tree position takes its tree_slots entry (a shift for a power-of-two
+    // page size).
+    auto win_len = [&](int w) { return min(ntiles * kTileKeys - w * kWinKeys, kWinKeys); };
+    // Window 0 with pages of at least 16 slots: the page entries it spans (at
+    // most 258) go straight to LDS, into the index ring's other half (idle
+    // until window 1, halfway through window 0), and so do the tree slots
+    // when the window reaches the tree block; no registers, so their round
+    // trip overlaps Q's loads. expand0 then forms the window's slots from LDS
+    // while Q's loads are still in flight: a few positions per thread,
+    // against the page arithmetic of sixteen.
+    constexpr int kTreeOff = kWinKeys - 64;  // tree slots' place in that half
+    auto stage_pages0 = [&]() {
+        if constexpr (kPaged) {
+            const int n = win_len(0);
+            const int ps = a.page_size;
+            const int t0 = S - N;
+            const int pg0 = k0 / ps;
+            const int count = k0 < t0 ? min(k0 + n - 1, t0 - 1) / ps - pg0 + 1 : 0;  // uniform
+            const int32_t* prow = a.prefix_pages + (int64_t)b * a.max_pages;
+            const uint32_t base = (uint32_t)(uintptr_t)(LDS_AS int*)s_idx[1];
+            for (int e = 0; e < count; e += kThreads)
+                gather4_to_lds(prow + min(pg0 + min(e + tid, count - 1), a.max_pages - 1),
+                               base + (e + wave * 64) * 4);
+            if (k0 + n > t0 && wave == 0)  // uniform: the window reaches the tree block
+                gather4_to_lds(a.tree_slots + (int64_t)b * N + min(lane, N - 1), base + kTreeOff * 4);
+        }
+    };
+    auto expand0 = [&]() {
+        if constexpr (kPaged) {
+            const int n = win_len(0);
+            const int ps = a.page_size;
+            const bool pow2 = (ps & (ps - 1)) == 0;
+            const int sh = __builtin_ctz((unsigned)ps);
+            const int t0 = S - N;
+            const int pg0 = k0 / ps;
+            for (int i = tid; i < n; i += kThreads) {
+                const int p = min(k0 + i, S - 1);
+                int64_t v;
+                if (p < t0) {
+                    const int pg = pow2 ? (p >> sh) : p / ps;
+                    v = (int64_t)s_idx[1][pg - pg0] * ps + (p - pg * ps);
+                } else {
+                    v = s_idx[1][kTreeOff + (p - t0)];
+                }
+                s_idx[0][i] = (int)(v < 0 ? 0 : (v > maxslot ? maxslot : v));  // clamped to the pool
+            }
+        }
+    };
     auto stage = [&](int w) {
         const int n = min(ntiles * kTileKeys - w * kWinKeys, kWinKeys);
         if constexpr (kPaged) {
-            // Hybrid layout: a prefix position p takes page p / page_size of
-            // its row (a page number past the row reads the last entry) plus
-            // p % page_size; a tree position takes its tree_slots entry. Every
-            // entry of this thread's positions is loaded first, so the window
-            // costs one round trip (a shift for a power-of-two page size).
+            // Windows after the first, and window 0 with pages under 16 slots:
+            // every entry of this thread's positions is loaded first, so the
+            // window costs one round trip.
             constexpr int kPer = kWinKeys / kThreads;
             const int ps = a.page_size;
             const bool pow2 = (ps & (ps - 1)) == 0;
@@ -463,7 +511,11 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(Args a, int slots, i
                 gather4_to_lds(pt + min(k0 + w * kWinKeys + i + tid, S - 1), dst + i * 4);
         }
     };
-    stage(0);
+    const bool pages0 = kPaged && a.page_size >= 16;  // uniform
+    if (pages0)
+        stage_pages0();
+    else
+        stage(0);
 
     // This lane's query row in each row block: fragments of Q as the B operand
     // of S^T = K.Q^T, and the tree-mask words of the row's node.
@@ -488,6 +540,16 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(Args a, int slots, i
         mw1[rb] = W > 1 ? mrow[1] : 0u;
     }
     const int tree0 = S - N;  // first key position holding a tree node
+    if (pages0) {
+        // The page entries are older than Q's 18 loads and the mask words (at
+        // least 19 operations, in order), so this waits for the entries only;
+        // the expansion then runs while Q's loads are in flight, and the
+        // barrier below publishes its slots.
+        static_assert(kKSteps == 18, "Q's loads per row block");
+        wait_vmcnt<19>();
+        __syncthreads();
+        expand0();
+    }
 
     const uint32_t lds0 = (uint32_t)(uintptr_t)(LDS_AS char*)s_kv;
     const char* kv = (const char*)a.kv;
