@@ -64,27 +64,55 @@ __device__ __forceinline__ void wait_vmcnt()
     __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
-// One wave-wide 16-byte-per-lane gather straight into LDS: lane i's 16 bytes
-// land at lds_addr + 16 * i (lds_addr wave-uniform, in M0). Issued as inline
-// assembly so that the compiler's wait insertion does not treat every later LDS
-// read as dependent on it; completion is tracked by the explicit vmcnt waits in
-// the tile loop, and the "memory" clobber keeps LDS accesses in program order.
-// M0 is written here and nowhere else in these kernels (gfx9 LDS instructions
-// do not read it), so clobbering it loses nothing.
+// Gathers straight into LDS are issued as inline assembly so that the
+// compiler's wait insertion does not treat every later LDS read as dependent
+// on them; their completion is tracked by the explicit vmcnt waits in the tile
+// loop, and the "memory" clobber keeps LDS accesses in program order. The LDS
+// destination is M0 plus the instruction offset (which moves the global
+// address alike) plus the lane's index times the load size; nothing else in
+// these kernels reads M0 (gfx9 LDS instructions do not).
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
-__device__ __forceinline__ void gather16_to_lds(const void* src, uint32_t lds_addr)
+// Gather j (0..8) of a tile's row plan into the tile slot at slot_lds (wave
+// uniform): lane i's 16 bytes land at slot_lds + 1024 j + 16 i. The gathers of
+// a group of four share one M0 value, slot_lds + 4096 (j / 4), and take
+// instruction offsets 1024 (j % 4); src is therefore the row address minus
+// 1024 (j % 4), which the row plan folds into its byte offsets. M0 is an input
+// operand, so the compiler writes it only when its value changes (one write
+// per group instead of one per gather); the s_nop is the wait state an M0
+// write needs before a load to LDS.
+template <int kSub>
+__device__ __forceinline__ void gather16_off(const void* src, uint32_t m0v)
 {
-    // lds_addr is wave-uniform by contract; readfirstlane puts it in a scalar
-    // register even where the compiler cannot prove the uniformity itself
-    const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds_addr);
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off offset:%2"
                  :
-                 : "v"(src), "s"(m0v)
-                 : "memory", "m0");
+                 : "v"(src), "{m0}"(m0v), "i"(kSub * 1024)
+                 : "memory");
+}
+__device__ __forceinline__ void gather16_slot(const void* src_minus_sub, uint32_t slot_lds, int j)
+{
+    // readfirstlane keeps the value in a scalar register even where the
+    // compiler cannot prove it uniform
+    const uint32_t m0v = __builtin_amdgcn_readfirstlane(slot_lds + (uint32_t)(j >> 2) * 4096u);
+    switch (j & 3) {  // j is a constant after unrolling
+    case 0: gather16_off<0>(src_minus_sub, m0v); break;
+    case 1: gather16_off<1>(src_minus_sub, m0v); break;
+    case 2: gather16_off<2>(src_minus_sub, m0v); break;
+    default: gather16_off<3>(src_minus_sub, m0v); break;
+    }
 }
 
-// The same for one 4-byte word per lane: lane i's word lands at lds_addr + 4 * i.
+// clamp(x, 0, hi) for hi >= 0, in one instruction
+__device__ __forceinline__ int clamp_slot(int x, int hi)
+{
+    int r;
+    asm("v_med3_i32 %0, %1, 0, %2" : "=v"(r) : "v"(x), "v"(hi));
+    return r;
+}
+
+// One 4-byte word per lane: lane i's word lands at lds_addr + 4 * i (lds_addr
+// wave uniform). It sets M0 itself and declares the clobber, so a later
+// gather16_slot has the compiler write M0 again.
 __device__ __forceinline__ void gather4_to_lds(const void* src, uint32_t lds_addr)
 {
     const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds_addr);
@@ -563,18 +591,25 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(Args a, int slots, i
     // (opaque_plan), so that the unpacking and the row addresses derived from
     // it are formed in the loop rather than kept live across it: that leaves
     // room for the second block's Q and O.
+    // gcs[j]: the byte offset less 1024 (j % 4) (see gather16_slot); packed
+    // with the row as (gcs + 3072) | row << 16, the low half non-negative.
     int gkl[kLoadsPerWave];
-    int gco[kLoadsPerWave];
+    int gcs[kLoadsPerWave];
     int gpk[kLoadsPerWave];
 #pragma unroll
     for (int j = 0; j < kLoadsPerWave; ++j) {
         const int z = j * 64 + lane;
         gkl[j] = z / kChunks;
-        gco[j] = ((z - gkl[j] * kChunks) ^ swz(gkl[j])) * 16;
-        gpk[j] = gco[j] | (gkl[j] << 16);
+        gcs[j] = ((z - gkl[j] * kChunks) ^ swz(gkl[j])) * 16 - (j & 3) * 1024;
+        gpk[j] = (gcs[j] + 3072) | (gkl[j] << 16);
     }
     auto g_kl = [&](int j) { return kRB == 1 ? gkl[j] : gpk[j] >> 16; };
-    auto g_co = [&](int j) { return kRB == 1 ? gco[j] : gpk[j] & 0xffff; };
+    // kv plus the gather's row-independent byte offset (less 1024 (j % 4))
+    const char* kv_m3k = kv - 3072;
+    auto g_src = [&](int j, int slot) {
+        return kRB == 1 ? kv + (int64_t)slot * kRowBytes + gcs[j]
+                        : kv_m3k + (int64_t)slot * kRowBytes + (gpk[j] & 0xffff);
+    };
     auto opaque_plan = [&]() {
         if constexpr (kRB > 1)
             asm volatile(""
@@ -592,14 +627,14 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(Args a, int slots, i
         const int* tidx = &s_idx[(t / kWinTiles) & 1][(t % kWinTiles) * kTileKeys + wave * kKeysPerWave];
 #pragma unroll
         for (int j = 0; j < kLoadsPerWave; ++j)
-            out[j] = min(max(tidx[g_kl(j)], 0), maxslot);  // slots clamped to the pool
+            out[j] = clamp_slot(tidx[g_kl(j)], maxslot);  // slots clamped to the pool
     };
     auto issue = [&](int t, const int* idx) {
         const uint32_t dst = lds0 + (uint32_t)((t % kStages) * kTileBytes +
                                                wave * (kKeysPerWave * kRowBytes));
 #pragma unroll
         for (int j = 0; j < kLoadsPerWave; ++j)
-            gather16_to_lds(kv + (int64_t)idx[j] * kRowBytes + g_co(j), dst + j * 1024);
+            gather16_slot(g_src(j, idx[j]), dst, j);
     };
 
     // Per-lane LDS byte offsets inside a tile buffer; everything else is an
@@ -707,6 +742,9 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(Args a, int slots, i
     };
 
     int t = 0;
+    // byte offsets of tile t's buffer and of the one tile t+2 gathers into,
+    // (t % 3) and ((t + 2) % 3) buffers, advanced with t
+    int cur_off = 0, gat_off = 2 * kTileBytes;
     next_tile(0);
     if constexpr (kRB > 1) {
         // Every row's first reference comes from tile 0's scores, computed
@@ -758,7 +796,8 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(Args a, int slots, i
             wait_vmcnt<0>();
         for (;;) {
             opaque_plan();
-            const char LDS_AS* buf = (const char LDS_AS*)s_kv + (t % kStages) * kTileBytes;
+            static_assert(kStages == 3, "the ring offsets rotate over three buffers");
+            const char LDS_AS* buf = (const char LDS_AS*)s_kv + cur_off;
             const char LDS_AS* kb0 = buf + koff0;
             const char LDS_AS* kb1 = buf + koff1;
             const int base = k0 + t * kTileKeys;
@@ -770,8 +809,7 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(Args a, int slots, i
             // from the last staged indices into that free buffer: identical or
             // never-read bytes, rows already in L2, and waits that only get
             // stricter.
-            const uint32_t gdst = lds0 + (uint32_t)(((t + 2) % kStages) * kTileBytes +
-                                                    wave * (kKeysPerWave * kRowBytes));
+            const uint32_t gdst = lds0 + (uint32_t)(gat_off + wave * (kKeysPerWave * kRowBytes));
 
             // S^T = K.Q^T for key blocks 0 and 1 (keys kb*16 + 4*lg + i against
             // row rl), two interleaved MFMA chains fed by double-buffered groups
@@ -797,7 +835,7 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(Args a, int slots, i
                             *(const bf16x8 LDS_AS*)kptr((g + 1) * kKGroup + j);
                 }
                 if (g < kLoadsPerWave)
-                    gather16_to_lds(kv + (int64_t)idx_n[g] * kRowBytes + g_co(g), gdst + g * 1024);
+                    gather16_slot(g_src(g, idx_n[g]), gdst, g);
 #pragma unroll
                 for (int j = 0; j < kKGroup; ++j) {
                     const int n = g * kKGroup + j;
@@ -888,7 +926,7 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(Args a, int slots, i
                     constexpr int kVGs = kColBlocks / kVGroup;
 #pragma unroll
                     for (int j = kKGroups + g * kRest / kVGs; j < kKGroups + (g + 1) * kRest / kVGs; ++j)
-                        gather16_to_lds(kv + (int64_t)idx_n[j] * kRowBytes + g_co(j), gdst + j * 1024);
+                        gather16_slot(g_src(j, idx_n[j]), gdst, j);
                 }
 #pragma unroll
                 for (int c = 0; c < kVGroup; ++c) {
@@ -908,6 +946,8 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(Args a, int slots, i
                 __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
             }
             __builtin_amdgcn_sched_group_barrier(0x008, kVGroup * kRB, 1);
+            gat_off = cur_off;
+            cur_off = cur_off == 2 * kTileBytes ? 0 : cur_off + kTileBytes;
             if (++t >= ntiles) {
                 // The two-row-block form leaves straight for the stores: a
                 // shared exit with the raise path below would run that path's
