@@ -82,14 +82,14 @@ __device__ __forceinline__ void wait_vmcnt()
 // per group instead of one per gather); the s_nop is the wait state an M0
 // write needs before a load to LDS.
 template <int kSub>
-__device__ __forceinline__ void gather16_off(const void* src, uint32_t m0v)
+__device__ __forceinline__ void gather16_off(uint64_t src, uint32_t m0v)
 {
     asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off offset:%2"
                  :
                  : "v"(src), "{m0}"(m0v), "i"(kSub * 1024)
                  : "memory");
 }
-__device__ __forceinline__ void gather16_slot(const void* src_minus_sub, uint32_t slot_lds, int j)
+__device__ __forceinline__ void gather16_slot(uint64_t src_minus_sub, uint32_t slot_lds, int j)
 {
     // readfirstlane keeps the value in a scalar register even where the
     // compiler cannot prove it uniform
@@ -604,11 +604,13 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(Args a, int slots, i
         gpk[j] = (gcs[j] + 3072) | (gkl[j] << 16);
     }
     auto g_kl = [&](int j) { return kRB == 1 ? gkl[j] : gpk[j] >> 16; };
-    // kv plus the gather's row-independent byte offset (less 1024 (j % 4))
-    const char* kv_m3k = kv - 3072;
+    // The gather's address less 1024 (j % 4), as an integer: it can lie below
+    // the pool's start and is only formed, never read, before the instruction
+    // offset is added back.
+    const uint64_t kv_addr = (uint64_t)(uintptr_t)kv;
     auto g_src = [&](int j, int slot) {
-        return kRB == 1 ? kv + (int64_t)slot * kRowBytes + gcs[j]
-                        : kv_m3k + (int64_t)slot * kRowBytes + (gpk[j] & 0xffff);
+        return kRB == 1 ? kv_addr + (uint64_t)((int64_t)slot * kRowBytes + gcs[j])
+                        : kv_addr - 3072u + (uint64_t)((int64_t)slot * kRowBytes + (gpk[j] & 0xffff));
     };
     auto opaque_plan = [&]() {
         if constexpr (kRB > 1)
