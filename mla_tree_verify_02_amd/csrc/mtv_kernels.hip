@@ -17,6 +17,10 @@
 //   Slices have one length for the whole batch, derived on the device from
 //   seq_lens (slicing()), so a long sequence gets many and a short one few.
 //   Partial results go out with device-scope stores (through the XCD's L2).
+//   The 64-row form runs for hybrid paging; per-token calls with one row
+//   group per workgroup run split_ws_kernel instead, the same computation
+//   with 8 waves: 4 compute the scores and weights, 4 the weighted values,
+//   two waves per SIMD.
 // combine_kernel: merges the slices of each row by log-sum-exp and writes the
 //   bf16 output and the natural-log lse; one workgroup per work item, or, for
 //   batches of 2..64 sequences, a fixed grid that walks the items the batch
@@ -1089,6 +1093,429 @@ slice_done:
     }
 }
 
+// Split kernel with the work of one 64-row group divided between two kinds of
+// wave, two waves per SIMD (per-token table, one 16-row block per wave):
+// - score waves (0..3) hold Q for their 16 rows, read K from LDS, compute
+//   S^T = K.Q^T, mask, keep the running max and sum, and publish the bf16
+//   weights P of a tile in LDS;
+// - value waves (4..7) each hold O for all 64 rows and 128 of the 512
+//   columns, gather the rows of later tiles and stage the index windows, and
+//   accumulate O^T += V^T.P^T one tile behind the score waves. Split by
+//   columns, each value wave reads a quarter of the tile's V^T and the four
+//   row blocks' weights, and each V^T operand feeds four MFMAs: the tile's LDS
+//   reads of V fall to a quarter, and LDS bandwidth is what bounds the tile.
+// With one wave per SIMD the split kernel issues one instruction every few
+// clocks and cannot keep the matrix pipe busy; two waves per SIMD issue side
+// by side. After the index staging the arithmetic is that of
+// split_kernel<true, 1> (hybrid paging) in the same order, so a per-token call
+// and a paged call over the same rows give the same bits.
+//
+// Iteration i (0..ntiles) of both kinds starts at one barrier. Before it, the
+// value waves have waited for the gathers of tile i (only tile i+1's may still
+// be in flight) and the score waves have published P(i-1). After it, the score
+// waves work on tile i (ring slot i % 4) and the value waves on tile i-1 (slot
+// (i-1) % 4), and gather tile i+2 into slot (i+2) % 4, whose last readers
+// (tile i-2) finished before the barrier. P and the rescale flag of tile i
+// use buffer i % 2, read by the value waves in iteration i+1.
+constexpr int kWsThreads = 512;
+constexpr int kWsStages = 4;
+constexpr int kWsWinTiles = 16;                       // tiles per staged index window
+constexpr int kWsWinKeys = kWsWinTiles * kTileKeys;   // 512 page indices per window
+
+__global__ __launch_bounds__(kWsThreads, 1) void split_ws_kernel(Args a, int slots, int single_c,
+                                                                 int max_slices, int row_groups,
+                                                                 float scale_log2)
+{
+    __shared__ __attribute__((aligned(16))) char s_kv[kWsStages * kTileBytes];
+    __shared__ __attribute__((aligned(16))) int s_idx[2][kWsWinKeys];
+    __shared__ __attribute__((aligned(16))) bf16x8 s_p[2][kWaves][64];  // weights of a tile
+    __shared__ float s_alpha[2][kWaves][16];  // O rescale factors of a tile's rows
+    __shared__ int s_raise[2][kWaves];        // whether a tile rescales O
+    __shared__ int64_t s_red[kWsThreads / 64];
+    __shared__ int s_hit[3];
+
+    int64_t c, nslices, tb;
+    int sk;
+    slicing<kWsThreads>(a, slots, single_c, s_red, c, nslices, sk, tb);
+
+    // XCD-aware order, as in split_kernel (one row group per workgroup)
+    const int L = blockIdx.x;
+    const int items = (a.batch == 1 ? max_slices : (int)nslices) * row_groups;
+    const int per_xcd = xcd_block(items, row_groups);
+    const int item = (L & 7) * per_xcd + (L >> 3);
+    if ((L >> 3) >= per_xcd || item >= items)
+        return;  // the whole workgroup (every value above is uniform)
+    const int gslice = item / row_groups;
+    const int grp = item - gslice * row_groups;
+    const int tid = threadIdx.x;
+
+    int b = 0;
+    int split = gslice;
+    int S = sk;
+    if (a.batch == 1 && gslice >= nslices) {
+        // past a shorter sequence: the empty partial, (max, sum) = (-inf, 0), O = 0
+        const size_t pz = (size_t)grp * max_slices + gslice;
+        if (tid < kRowsPerGroup) {
+            float2* pm = (float2*)a.part_ml + pz * kRowsPerGroup + tid;
+            *pm = make_float2(-INFINITY, 0.f);
+        }
+        uint4* po = (uint4*)((__bf16*)a.part_o + pz * (size_t)(kRowsPerGroup * kPartRowElems));
+        for (int i = tid; i < kRowsPerGroup * kPartRowElems * 2 / 16; i += kWsThreads)
+            po[i] = uint4{0u, 0u, 0u, 0u};
+        return;  // the whole workgroup
+    }
+    if (__builtin_expect(a.batch > 1 && a.batch <= kWaveBatch, 0)) {
+        const int nl = (int)((tb + c - 1) / c);
+        const int incl = wave_incl_scan(nl);
+        const uint64_t hit = __builtin_amdgcn_ballot_w64(nl > 0 && gslice >= incl - nl && gslice < incl);
+        const int bl = __builtin_ctzll(hit);
+        b = bl;
+        split = gslice - (__shfl(incl, bl) - __shfl(nl, bl));
+        S = __shfl(sk, bl);
+    } else if (__builtin_expect(a.batch > kWaveBatch, 0)) {
+        if (tid == 0)
+            s_hit[0] = 0, s_hit[1] = 0, s_hit[2] = 0;
+        int64_t base = 0;
+        for (int b0 = 0; b0 < a.batch; b0 += kWsThreads) {
+            const int bb = b0 + tid;
+            int64_t n = 0;
+            if (a.batch <= kWsThreads)
+                n = (tb + c - 1) / c;
+            else if (bb < a.batch)
+                n = (seq_tiles(a, bb) + c - 1) / c;
+            int64_t tot;
+            const int64_t st = base + block_excl_scan<kWsThreads>(n, s_red, tot);
+            if (n > 0 && gslice >= st && gslice < st + n) {
+                s_hit[0] = bb;
+                s_hit[1] = (int)(gslice - st);
+                s_hit[2] = a.batch <= kWsThreads ? sk : seq_keys(a, bb);
+            }
+            base += tot;
+        }
+        __syncthreads();
+        b = s_hit[0];
+        split = s_hit[1];
+        S = s_hit[2];
+    }
+    b = __builtin_amdgcn_readfirstlane(b);
+    split = __builtin_amdgcn_readfirstlane(split);
+    S = __builtin_amdgcn_readfirstlane(S);
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const bool score = wave < kWaves;  // uniform
+    const int rw = wave & (kWaves - 1);  // 16-row block of this wave
+    const int rl = lane & 15;
+    const int lg = lane >> 4;
+    const int N = a.nodes;
+    const int H = a.heads;
+    const int R = N * H;
+
+    if (split == 0 && grp == 0 && tid == 0) {
+        const int tiles_b = (S + kTileKeys - 1) / kTileKeys;
+        a.seq_slices[2 * b] = gslice;
+        a.seq_slices[2 * b + 1] = (int)((tiles_b + c - 1) / c);
+    }
+    const int k0 = __builtin_amdgcn_readfirstlane((int)((int64_t)split * c * kTileKeys));
+    const int nkeys = __builtin_amdgcn_readfirstlane((int)min((int64_t)S - k0, c * kTileKeys));
+    const int ntiles = (nkeys + kTileKeys - 1) / kTileKeys;
+
+    // Index windows of 16 tiles: window w into s_idx[w % 2], staged by the value
+    // waves: window 0 before the first barrier, window w+1 at iteration 16w + 4,
+    // when the last reader of that half (tile 16w - 1, read at iteration
+    // 16w - 4) is past, and well before its first reader (iteration 16w + 13).
+    const int32_t* pt = a.page_table + (int64_t)b * a.max_kv;
+    const int maxslot = (int)(a.num_slots - 1);
+    const int nwin = (ntiles + kWsWinTiles - 1) / kWsWinTiles;
+    auto stage_win = [&](int w) {  // value waves only
+        const int n = min(ntiles * kTileKeys - w * kWsWinKeys, kWsWinKeys);
+        const uint32_t dst = (uint32_t)(uintptr_t)(LDS_AS int*)s_idx[w & 1] + rw * 256;
+        for (int i = 0; i < n; i += kWaves * 64)
+            gather4_to_lds(pt + min(k0 + w * kWsWinKeys + i + rw * 64 + lane, S - 1), dst + i * 4);
+    };
+
+    const int tree0 = S - N;
+    const uint32_t lds0 = (uint32_t)(uintptr_t)(LDS_AS char*)s_kv;
+    const uint64_t kv_addr = (uint64_t)(uintptr_t)a.kv;
+
+    if (score) {
+        // ------------------------------------------------ score waves
+        // This lane's Q fragments and the tree-mask words of its row, loaded
+        // while the value waves stage index window 0 (each kind keeps its own
+        // registers: nothing of one is live in the other's code).
+        const int W = (N + 31) >> 5;
+        const int row = grp * kRowsPerGroup + rw * 16 + rl;
+        bf16x8 qf[kKSteps];
+        uint32_t mw0, mw1;
+        {
+            const bool row_ok = row < R;
+            const __bf16* qrow = (const __bf16*)a.q + ((int64_t)b * R + (row_ok ? row : 0)) * kDqk;
+#pragma unroll
+            for (int s = 0; s < kKSteps; ++s) {
+                bf16x8 v = *(const bf16x8*)(qrow + (4 * s + lg) * 8);
+                if (!row_ok)
+                    v = bf16x8{};
+                qf[s] = v;
+            }
+            const int node = (row_ok ? row : 0) / H;
+            const uint32_t* mrow = a.tree_mask + ((int64_t)b * N + node) * W;
+            mw0 = mrow[0];
+            mw1 = W > 1 ? mrow[1] : 0u;
+        }
+        __syncthreads();  // index window 0 staged
+        const int fk = swz(rl);
+        const int koff0 = rl * kRowBytes + 16 * (lg ^ fk);
+        const int koff1 = rl * kRowBytes + 16 * ((4 + lg) ^ fk);
+        constexpr float kSlack = 16.0f;
+        float m_ref = -INFINITY, l_run = 0.f;
+        constexpr int kKGroup = 4;
+        constexpr int kKReads = 2 * kKSteps;
+        int cur_off = 0;
+        for (int i = 0; i <= ntiles; ++i) {
+            __syncthreads();  // tile i in LDS; the value waves are past P(i-2)
+            if (i == ntiles)
+                break;
+            const char LDS_AS* buf = (const char LDS_AS*)s_kv + cur_off;
+            const char LDS_AS* kb0 = buf + koff0;
+            const char LDS_AS* kb1 = buf + koff1;
+            const int base = k0 + i * kTileKeys;
+            auto kptr = [&](int n) {
+                const int s = n >> 1;
+                return ((s & 1) ? kb1 : kb0) + (n & 1) * 16 * kRowBytes + 128 * (s >> 1);
+            };
+            bf16x8 kf[2][kKGroup];
+#pragma unroll
+            for (int j = 0; j < kKGroup; ++j)
+                kf[0][j] = *(const bf16x8 LDS_AS*)kptr(j);
+            f32x4 sacc[2];
+            sacc[0] = sacc[1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int g = 0; g < kKReads / kKGroup; ++g) {
+                if (g + 1 < kKReads / kKGroup) {
+#pragma unroll
+                    for (int j = 0; j < kKGroup; ++j)
+                        kf[(g + 1) & 1][j] = *(const bf16x8 LDS_AS*)kptr((g + 1) * kKGroup + j);
+                }
+#pragma unroll
+                for (int j = 0; j < kKGroup; ++j) {
+                    const int n = g * kKGroup + j;
+                    sacc[n & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[g & 1][j], qf[n >> 1], sacc[n & 1], 0, 0, 0);
+                }
+            }
+            __builtin_amdgcn_sched_group_barrier(0x100, kKGroup, 0);
+#pragma unroll
+            for (int q = 0; q < kKReads - kKGroup; ++q) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, kKGroup, 0);
+            float x[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k)
+                x[k] = sacc[k >> 2][k & 3] * scale_log2;
+            if (base + kTileKeys > tree0) {
+#pragma unroll
+                for (int k = 0; k < 8; ++k) {
+                    const int p = base + (k >> 2) * 16 + 4 * lg + (k & 3);
+                    const int j = p - tree0;
+                    bool vis = p < tree0;
+                    if (p >= tree0 && p < S)
+                        vis = (((j < 32) ? mw0 : mw1) >> (j & 31)) & 1u;
+                    if (!vis)
+                        x[k] = -INFINITY;
+                }
+            }
+            float mt = x[0];
+#pragma unroll
+            for (int k = 1; k < 8; ++k)
+                mt = fmaxf(mt, x[k]);
+            const int pb_i = i & 1;
+            int raised = 0;
+            if (__builtin_amdgcn_ballot_w64(mt > m_ref + kSlack) != 0) {
+                // raise every row's reference to its running max; O is
+                // rescaled by the value wave before it adds this tile
+                float m = fmaxf(mt, __shfl_xor(mt, 16));
+                m = fmaxf(m, __shfl_xor(m, 32));
+                const float m_new = fmaxf(m_ref, m);
+                const float alpha = (m_ref == -INFINITY) ? 0.f : exp2f(m_ref - m_new);
+                m_ref = m_new;
+                l_run *= alpha;
+                if (lg == 0)
+                    s_alpha[pb_i][rw][rl] = alpha;
+                raised = 1;
+            }
+            if (lane == 0)
+                s_raise[pb_i][rw] = raised;
+            bf16x8 pb;
+            {
+                const float mr = (m_ref == -INFINITY) ? 0.f : m_ref;
+                float psum = 0.f;
+#pragma unroll
+                for (int k = 0; k < 8; ++k) {
+                    const float pk = __builtin_amdgcn_exp2f(x[k] - mr);
+                    psum += pk;
+                    pb[k] = (__bf16)pk;
+                }
+                l_run += psum;
+            }
+            s_p[pb_i][rw][lane] = pb;
+            cur_off = cur_off == (kWsStages - 1) * kTileBytes ? 0 : cur_off + kTileBytes;
+        }
+        // this slice's (max, sum) per row
+        float l_tot = l_run + __shfl_xor(l_run, 16);
+        l_tot += __shfl_xor(l_tot, 32);
+        if (lg == 0) {
+            const size_t pidx = (size_t)grp * max_slices + gslice;
+            float2* pm = (float2*)a.part_ml + pidx * kRowsPerGroup + rw * 16 + rl;
+            __hip_atomic_store((uint64_t*)pm, __builtin_bit_cast(uint64_t, make_float2(m_ref, l_tot)),
+                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        return;
+    }
+
+    // ---------------------------------------------------- value waves
+    stage_win(0);
+    wait_vmcnt<0>();
+    __syncthreads();  // index window 0 staged
+    int gcs[kLoadsPerWave];
+#pragma unroll
+    for (int j = 0; j < kLoadsPerWave; ++j) {
+        const int z = j * 64 + lane;
+        const int kl = z / kChunks;
+        gcs[j] = ((z - kl * kChunks) ^ swz(kl)) * 16 - (j & 3) * 1024;
+    }
+    int gkl[kLoadsPerWave];
+#pragma unroll
+    for (int j = 0; j < kLoadsPerWave; ++j)
+        gkl[j] = (j * 64 + lane) / kChunks;
+    auto g_src = [&](int j, int slot) { return kv_addr + (uint64_t)((int64_t)slot * kRowBytes + gcs[j]); };
+    auto load_idx = [&](int t, int* out) {
+        const int* tidx = &s_idx[(t / kWsWinTiles) & 1][(t % kWsWinTiles) * kTileKeys + rw * kKeysPerWave];
+#pragma unroll
+        for (int j = 0; j < kLoadsPerWave; ++j)
+            out[j] = clamp_slot(tidx[gkl[j]], maxslot);
+    };
+    auto slot_lds = [&](int t) {
+        return lds0 + (uint32_t)((t % kWsStages) * kTileBytes + rw * (kKeysPerWave * kRowBytes));
+    };
+    // Gathers go out for every iteration; past the last tile they repeat the
+    // last staged indices into a free slot (rows already fetched, never
+    // read), which keeps one wait count for every iteration.
+    int idx_n[kLoadsPerWave];
+    load_idx(0, idx_n);
+#pragma unroll
+    for (int j = 0; j < kLoadsPerWave; ++j)
+        gather16_slot(g_src(j, idx_n[j]), slot_lds(0), j);
+    if (ntiles > 1)
+        load_idx(1, idx_n);
+#pragma unroll
+    for (int j = 0; j < kLoadsPerWave; ++j)
+        gather16_slot(g_src(j, idx_n[j]), slot_lds(1), j);
+    if (ntiles > 2)
+        load_idx(2, idx_n);
+
+    const int vkey = 4 * lg + (rl >> 2);
+    const int fv = swz(vkey);
+    const int vsel = (rl & 3) >> 1;
+    int voff[4];
+#pragma unroll
+    for (int qd = 0; qd < 4; ++qd)
+        voff[qd] = vkey * kRowBytes + 16 * ((2 * qd + vsel) ^ fv) + (rl & 1) * 8;
+    // O^T of this wave's columns: column block cb0 + c (c = 0..7) for row block r
+    constexpr int kWsCols = kColBlocks / kWaves;  // 8 column blocks per value wave
+    const int cb0 = rw * kWsCols;
+    f32x4 o[kWaves][kWsCols];
+#pragma unroll
+    for (int r = 0; r < kWaves; ++r)
+#pragma unroll
+        for (int c = 0; c < kWsCols; ++c)
+            o[r][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // iteration 0: no P.V yet; the gathers of tile 2
+    wait_vmcnt<kLoadsPerWave>();
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < kLoadsPerWave; ++j)
+        gather16_slot(g_src(j, idx_n[j]), slot_lds(2), j);
+    if (3 < ntiles)
+        load_idx(3, idx_n);
+    for (int i = 1; i <= ntiles; ++i) {
+        // tile i landed: only tile i+1's gathers may be in flight
+        wait_vmcnt<kLoadsPerWave>();
+        __syncthreads();
+        if (i % kWsWinTiles == 4 && i / kWsWinTiles + 1 < nwin)
+            stage_win(i / kWsWinTiles + 1);
+        const uint32_t gdst = slot_lds(i + 2);
+        // P.V of tile i-1, after the rescales its scores asked for (rare);
+        // each value is multiplied in place, so that O keeps its registers.
+        const int pb_i = (i - 1) & 1;
+#pragma unroll
+        for (int r = 0; r < kWaves; ++r) {
+            if (__builtin_amdgcn_readfirstlane(s_raise[pb_i][r]) != 0) {
+                const float alpha = s_alpha[pb_i][r][rl];
+#pragma unroll
+                for (int c = 0; c < kWsCols; ++c)
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        float e = o[r][c][k];
+                        asm volatile("v_mul_f32 %0, %0, %1" : "+v"(e) : "v"(alpha));
+                        o[r][c][k] = e;
+                    }
+            }
+        }
+        bf16x8 pb[kWaves];
+#pragma unroll
+        for (int r = 0; r < kWaves; ++r)
+            pb[r] = s_p[pb_i][r][lane];
+        const char LDS_AS* buf = (const char LDS_AS*)s_kv + ((i - 1) % kWsStages) * kTileBytes;
+        auto vptr = [&](int cb) { return buf + voff[cb & 3] + 128 * (cb >> 2); };
+        // V^T operands two column blocks ahead of their MFMAs
+        bf16x4 vt[3][2];
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+            vt[c][0] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((bf16x4 LDS_AS*)vptr(cb0 + c));
+            vt[c][1] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((bf16x4 LDS_AS*)(vptr(cb0 + c) + 16 * kRowBytes));
+        }
+#pragma unroll
+        for (int c = 0; c < kWsCols; ++c) {
+            if (c + 2 < kWsCols) {
+                vt[(c + 2) % 3][0] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((bf16x4 LDS_AS*)vptr(cb0 + c + 2));
+                vt[(c + 2) % 3][1] =
+                    __builtin_amdgcn_ds_read_tr16_b64_v4bf16((bf16x4 LDS_AS*)(vptr(cb0 + c + 2) + 16 * kRowBytes));
+            }
+            // the nine gathers of tile i+2, spread over the eight column blocks
+#pragma unroll
+            for (int j = c * kLoadsPerWave / kWsCols; j < (c + 1) * kLoadsPerWave / kWsCols; ++j)
+                gather16_slot(g_src(j, idx_n[j]), gdst, j);
+            const bf16x8 va = __builtin_shufflevector(vt[c % 3][0], vt[c % 3][1], 0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+            for (int r = 0; r < kWaves; ++r)
+                o[r][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[r], o[r][c], 0, 0, 0);
+        }
+        if (i + 3 < ntiles)
+            load_idx(i + 3, idx_n);
+    }
+    // this slice's O, rounded to bf16, in the register-fragment order of the
+    // row blocks
+    const size_t pidx = (size_t)grp * max_slices + gslice;
+#pragma unroll
+    for (int r = 0; r < kWaves; ++r) {
+        __bf16* po = (__bf16*)a.part_o + pidx * (size_t)(kRowsPerGroup * kPartRowElems) +
+                     (size_t)r * (kColBlocks * 64 * 4);
+#pragma unroll
+        for (int c = 0; c < kWsCols; ++c) {
+            bf16x4 v;
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+                v[k] = (__bf16)o[r][c][k];
+            __hip_atomic_store((uint64_t*)(po + ((cb0 + c) * 64 + lane) * 4), __builtin_bit_cast(uint64_t, v),
+                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+    // The last gathers write LDS, so they land before the workgroup ends; the
+    // 32 stores are younger, and vmcnt retires in order.
+    wait_vmcnt<kColBlocks>();
+}
+
 // Merge of one (sequence b, 16-row block rb, group xblk of column units) by
 // the workgroup's 8 waves. A unit is a 16-column block (kVals = 4: a lane
 // holds the 4 values of one fragment lane) or half of one (kVals = 2: 8
@@ -1294,8 +1721,14 @@ hipError_t launch_split(const Plan& p, const Args& a, hipStream_t stream)
     // pairs them with the hybrid layout)
     if (p.rb == 2 && a.prefix_pages)
         return hipErrorInvalidValue;
-    auto kernel = p.rb == 2 ? split_kernel<false, 2>
-                            : (a.prefix_pages ? split_kernel<true, 1> : split_kernel<false, 1>);
+    // one row block per wave with a per-token table: score and value waves,
+    // two per SIMD
+    if (p.rb == 1 && !a.prefix_pages) {
+        hipLaunchKernelGGL(split_ws_kernel, dim3(8 * per_xcd), dim3(kWsThreads), 0, stream, a, p.slots,
+                           p.single_c, p.max_slices, p.row_groups, scale_log2);
+        return hipGetLastError();
+    }
+    auto kernel = p.rb == 2 ? split_kernel<false, 2> : split_kernel<true, 1>;
     hipLaunchKernelGGL(kernel, dim3(8 * per_xcd),
                        dim3(kThreads), 0, stream, a, p.slots, p.single_c, p.max_slices, p.row_groups,
                        scale_log2);
