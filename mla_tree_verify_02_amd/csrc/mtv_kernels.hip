@@ -68,6 +68,19 @@ __device__ __forceinline__ void wait_vmcnt()
     __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
+// The same with every LDS operation of the wave completed as well. Used before
+// a barrier that publishes this wave's LDS writes (ds_write) to other waves
+// while its direct-to-LDS gathers are in flight: __syncthreads() alone emits
+// no LDS wait here, and a wave that wrote a tile's rescale flag just before
+// the barrier was measured to leave it unseen by the reader after it (wrong
+// output in about 1 of 9 calls made right after the GPU had been idle).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_lds()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (0 << 8) | ((N >> 4) << 14));
+}
+
 // Gathers straight into LDS are issued as inline assembly so that the
 // compiler's wait insertion does not treat every later LDS read as dependent
 // on them; their completion is tracked by the explicit vmcnt waits in the tile
@@ -686,8 +699,8 @@ __global__ __launch_bounds__(kThreads, 1) void split_kernel(Args a, int slots, i
     // outstanding vector-memory operations are this wave's gathers (and, on
     // slices longer than a window, the reads of the next window, which the
     // waits below only make stricter).
-    wait_vmcnt<0>();
-    __syncthreads();  // index window 0 staged
+    wait_vmcnt_lds<0>();  // and the slots expanded in LDS are written
+    __syncthreads();      // index window 0 staged
     int idx_n[kLoadsPerWave];  // page indices of the next tile to gather
     load_idx(0, idx_n);
     issue(0, idx_n);
@@ -1095,12 +1108,13 @@ slice_done:
 
 // Split kernel with the work of one 64-row group divided between two kinds of
 // wave, two waves per SIMD (per-token table, one 16-row block per wave):
-// - score waves (0..3) hold Q for their 16 rows, read K from LDS, compute
-//   S^T = K.Q^T, mask, keep the running max and sum, and publish the bf16
-//   weights P of a tile in LDS;
+// - score waves (0..3) hold Q for their 16 rows, stage the index windows and
+//   gather the rows of later tiles, read K from LDS, compute S^T = K.Q^T,
+//   mask, keep the running max and sum, and publish the bf16 weights P of a
+//   tile in LDS;
 // - value waves (4..7) each hold O for all 64 rows and 128 of the 512
-//   columns, gather the rows of later tiles and stage the index windows, and
-//   accumulate O^T += V^T.P^T one tile behind the score waves. Split by
+//   columns and accumulate O^T += V^T.P^T one tile behind the score waves,
+//   with no global memory traffic until their final stores. Split by
 //   columns, each value wave reads a quarter of the tile's V^T and the four
 //   row blocks' weights, and each V^T operand feeds four MFMAs: the tile's LDS
 //   reads of V fall to a quarter, and LDS bandwidth is what bounds the tile.
@@ -1111,12 +1125,12 @@ slice_done:
 // and a paged call over the same rows give the same bits.
 //
 // Iteration i (0..ntiles) of both kinds starts at one barrier. Before it, the
-// value waves have waited for the gathers of tile i (only tile i+1's may still
-// be in flight) and the score waves have published P(i-1). After it, the score
-// waves work on tile i (ring slot i % 4) and the value waves on tile i-1 (slot
-// (i-1) % 4), and gather tile i+2 into slot (i+2) % 4, whose last readers
-// (tile i-2) finished before the barrier. P and the rescale flag of tile i
-// use buffer i % 2, read by the value waves in iteration i+1.
+// score waves have waited for the gathers of tile i (only tile i+1's may still
+// be in flight) and published P(i-1). After it, the score waves work on tile i
+// (ring slot i % 4) and gather tile i+2 into slot (i+2) % 4, whose last
+// readers (tile i-2) finished before the barrier; the value waves work on
+// tile i-1 (slot (i-1) % 4). P and the rescale flag of tile i use buffer
+// i % 2, read by the value waves in iteration i+1.
 constexpr int kWsThreads = 512;
 constexpr int kWsStages = 4;
 constexpr int kWsWinTiles = 16;                       // tiles per staged index window
@@ -1219,14 +1233,14 @@ __global__ __launch_bounds__(kWsThreads, 1) void split_ws_kernel(Args a, int slo
     const int nkeys = __builtin_amdgcn_readfirstlane((int)min((int64_t)S - k0, c * kTileKeys));
     const int ntiles = (nkeys + kTileKeys - 1) / kTileKeys;
 
-    // Index windows of 16 tiles: window w into s_idx[w % 2], staged by the value
+    // Index windows of 16 tiles: window w into s_idx[w % 2], staged by the score
     // waves: window 0 before the first barrier, window w+1 at iteration 16w + 4,
     // when the last reader of that half (tile 16w - 1, read at iteration
     // 16w - 4) is past, and well before its first reader (iteration 16w + 13).
     const int32_t* pt = a.page_table + (int64_t)b * a.max_kv;
     const int maxslot = (int)(a.num_slots - 1);
     const int nwin = (ntiles + kWsWinTiles - 1) / kWsWinTiles;
-    auto stage_win = [&](int w) {  // value waves only
+    auto stage_win = [&](int w) {  // score waves only
         const int n = min(ntiles * kTileKeys - w * kWsWinKeys, kWsWinKeys);
         const uint32_t dst = (uint32_t)(uintptr_t)(LDS_AS int*)s_idx[w & 1] + rw * 256;
         for (int i = 0; i < n; i += kWaves * 64)
@@ -1239,13 +1253,13 @@ __global__ __launch_bounds__(kWsThreads, 1) void split_ws_kernel(Args a, int slo
 
     if (score) {
         // ------------------------------------------------ score waves
-        // This lane's Q fragments and the tree-mask words of its row, loaded
-        // while the value waves stage index window 0 (each kind keeps its own
-        // registers: nothing of one is live in the other's code).
+        // Q fragments and tree-mask words of this lane's row; index window 0
+        // (this kind stages the windows, gathers the rows and waits for them)
         const int W = (N + 31) >> 5;
         const int row = grp * kRowsPerGroup + rw * 16 + rl;
         bf16x8 qf[kKSteps];
         uint32_t mw0, mw1;
+        stage_win(0);
         {
             const bool row_ok = row < R;
             const __bf16* qrow = (const __bf16*)a.q + ((int64_t)b * R + (row_ok ? row : 0)) * kDqk;
@@ -1261,7 +1275,44 @@ __global__ __launch_bounds__(kWsThreads, 1) void split_ws_kernel(Args a, int slo
             mw0 = mrow[0];
             mw1 = W > 1 ? mrow[1] : 0u;
         }
+        wait_vmcnt<0>();
         __syncthreads();  // index window 0 staged
+
+        // Gather plan: wave rw fills rows 8 rw .. 8 rw + 7 of each tile.
+        int gcs[kLoadsPerWave];
+        int gkl[kLoadsPerWave];
+#pragma unroll
+        for (int j = 0; j < kLoadsPerWave; ++j) {
+            const int z = j * 64 + lane;
+            gkl[j] = z / kChunks;
+            gcs[j] = ((z - gkl[j] * kChunks) ^ swz(gkl[j])) * 16 - (j & 3) * 1024;
+        }
+        auto g_src = [&](int j, int slot) { return kv_addr + (uint64_t)((int64_t)slot * kRowBytes + gcs[j]); };
+        auto load_idx = [&](int t, int* out) {
+            const int* tidx = &s_idx[(t / kWsWinTiles) & 1][(t % kWsWinTiles) * kTileKeys + rw * kKeysPerWave];
+#pragma unroll
+            for (int j = 0; j < kLoadsPerWave; ++j)
+                out[j] = clamp_slot(tidx[gkl[j]], maxslot);
+        };
+        auto slot_lds = [&](int t) {
+            return lds0 + (uint32_t)((t % kWsStages) * kTileBytes + rw * (kKeysPerWave * kRowBytes));
+        };
+        // Gathers go out for every iteration; past the last tile they repeat the
+        // last staged indices into a free slot (rows already fetched, never
+        // read), which keeps one wait count for every iteration.
+        int idx_n[kLoadsPerWave];
+        load_idx(0, idx_n);
+#pragma unroll
+        for (int j = 0; j < kLoadsPerWave; ++j)
+            gather16_slot(g_src(j, idx_n[j]), slot_lds(0), j);
+        if (ntiles > 1)
+            load_idx(1, idx_n);
+#pragma unroll
+        for (int j = 0; j < kLoadsPerWave; ++j)
+            gather16_slot(g_src(j, idx_n[j]), slot_lds(1), j);
+        if (ntiles > 2)
+            load_idx(2, idx_n);
+
         const int fk = swz(rl);
         const int koff0 = rl * kRowBytes + 16 * (lg ^ fk);
         const int koff1 = rl * kRowBytes + 16 * ((4 + lg) ^ fk);
@@ -1269,11 +1320,19 @@ __global__ __launch_bounds__(kWsThreads, 1) void split_ws_kernel(Args a, int slo
         float m_ref = -INFINITY, l_run = 0.f;
         constexpr int kKGroup = 4;
         constexpr int kKReads = 2 * kKSteps;
+        static_assert(kKReads / kKGroup == kLoadsPerWave, "one gather per K-operand group");
         int cur_off = 0;
         for (int i = 0; i <= ntiles; ++i) {
-            __syncthreads();  // tile i in LDS; the value waves are past P(i-2)
+            // tile i landed (only tile i+1's gathers may be in flight) and
+            // P(i-1) with its rescale flag and factors is written; the value
+            // waves are past P(i-2)
+            wait_vmcnt_lds<kLoadsPerWave>();
+            __syncthreads();
             if (i == ntiles)
                 break;
+            if (i % kWsWinTiles == 4 && i / kWsWinTiles + 1 < nwin)
+                stage_win(i / kWsWinTiles + 1);
+            const uint32_t gdst = slot_lds(i + 2);
             const char LDS_AS* buf = (const char LDS_AS*)s_kv + cur_off;
             const char LDS_AS* kb0 = buf + koff0;
             const char LDS_AS* kb1 = buf + koff1;
@@ -1295,6 +1354,8 @@ __global__ __launch_bounds__(kWsThreads, 1) void split_ws_kernel(Args a, int slo
                     for (int j = 0; j < kKGroup; ++j)
                         kf[(g + 1) & 1][j] = *(const bf16x8 LDS_AS*)kptr((g + 1) * kKGroup + j);
                 }
+                // gather g of tile i+2 (into the slot tile i-2 used)
+                gather16_slot(g_src(g, idx_n[g]), gdst, g);
 #pragma unroll
                 for (int j = 0; j < kKGroup; ++j) {
                     const int n = g * kKGroup + j;
@@ -1332,7 +1393,7 @@ __global__ __launch_bounds__(kWsThreads, 1) void split_ws_kernel(Args a, int slo
             int raised = 0;
             if (__builtin_amdgcn_ballot_w64(mt > m_ref + kSlack) != 0) {
                 // raise every row's reference to its running max; O is
-                // rescaled by the value wave before it adds this tile
+                // rescaled by the value waves before they add this tile
                 float m = fmaxf(mt, __shfl_xor(mt, 16));
                 m = fmaxf(m, __shfl_xor(m, 32));
                 const float m_new = fmaxf(m_ref, m);
@@ -1358,11 +1419,15 @@ __global__ __launch_bounds__(kWsThreads, 1) void split_ws_kernel(Args a, int slo
                 l_run += psum;
             }
             s_p[pb_i][rw][lane] = pb;
+            if (i + 3 < ntiles)
+                load_idx(i + 3, idx_n);
             cur_off = cur_off == (kWsStages - 1) * kTileBytes ? 0 : cur_off + kTileBytes;
         }
-        // this slice's (max, sum) per row
+        // this slice's (max, sum) per row; the last (repeated) gathers land
+        // first, so that no LDS write outlives the workgroup
         float l_tot = l_run + __shfl_xor(l_run, 16);
         l_tot += __shfl_xor(l_tot, 32);
+        wait_vmcnt<0>();
         if (lg == 0) {
             const size_t pidx = (size_t)grp * max_slices + gslice;
             float2* pm = (float2*)a.part_ml + pidx * kRowsPerGroup + rw * 16 + rl;
@@ -1373,46 +1438,7 @@ __global__ __launch_bounds__(kWsThreads, 1) void split_ws_kernel(Args a, int slo
     }
 
     // ---------------------------------------------------- value waves
-    stage_win(0);
-    wait_vmcnt<0>();
     __syncthreads();  // index window 0 staged
-    int gcs[kLoadsPerWave];
-#pragma unroll
-    for (int j = 0; j < kLoadsPerWave; ++j) {
-        const int z = j * 64 + lane;
-        const int kl = z / kChunks;
-        gcs[j] = ((z - kl * kChunks) ^ swz(kl)) * 16 - (j & 3) * 1024;
-    }
-    int gkl[kLoadsPerWave];
-#pragma unroll
-    for (int j = 0; j < kLoadsPerWave; ++j)
-        gkl[j] = (j * 64 + lane) / kChunks;
-    auto g_src = [&](int j, int slot) { return kv_addr + (uint64_t)((int64_t)slot * kRowBytes + gcs[j]); };
-    auto load_idx = [&](int t, int* out) {
-        const int* tidx = &s_idx[(t / kWsWinTiles) & 1][(t % kWsWinTiles) * kTileKeys + rw * kKeysPerWave];
-#pragma unroll
-        for (int j = 0; j < kLoadsPerWave; ++j)
-            out[j] = clamp_slot(tidx[gkl[j]], maxslot);
-    };
-    auto slot_lds = [&](int t) {
-        return lds0 + (uint32_t)((t % kWsStages) * kTileBytes + rw * (kKeysPerWave * kRowBytes));
-    };
-    // Gathers go out for every iteration; past the last tile they repeat the
-    // last staged indices into a free slot (rows already fetched, never
-    // read), which keeps one wait count for every iteration.
-    int idx_n[kLoadsPerWave];
-    load_idx(0, idx_n);
-#pragma unroll
-    for (int j = 0; j < kLoadsPerWave; ++j)
-        gather16_slot(g_src(j, idx_n[j]), slot_lds(0), j);
-    if (ntiles > 1)
-        load_idx(1, idx_n);
-#pragma unroll
-    for (int j = 0; j < kLoadsPerWave; ++j)
-        gather16_slot(g_src(j, idx_n[j]), slot_lds(1), j);
-    if (ntiles > 2)
-        load_idx(2, idx_n);
-
     const int vkey = 4 * lg + (rl >> 2);
     const int fv = swz(vkey);
     const int vsel = (rl & 3) >> 1;
@@ -1430,21 +1456,9 @@ __global__ __launch_bounds__(kWsThreads, 1) void split_ws_kernel(Args a, int slo
         for (int c = 0; c < kWsCols; ++c)
             o[r][c] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // iteration 0: no P.V yet; the gathers of tile 2
-    wait_vmcnt<kLoadsPerWave>();
-    __syncthreads();
-#pragma unroll
-    for (int j = 0; j < kLoadsPerWave; ++j)
-        gather16_slot(g_src(j, idx_n[j]), slot_lds(2), j);
-    if (3 < ntiles)
-        load_idx(3, idx_n);
+    __syncthreads();  // iteration 0: the score waves work on tile 0
     for (int i = 1; i <= ntiles; ++i) {
-        // tile i landed: only tile i+1's gathers may be in flight
-        wait_vmcnt<kLoadsPerWave>();
-        __syncthreads();
-        if (i % kWsWinTiles == 4 && i / kWsWinTiles + 1 < nwin)
-            stage_win(i / kWsWinTiles + 1);
-        const uint32_t gdst = slot_lds(i + 2);
+        __syncthreads();  // P(i-1) published
         // P.V of tile i-1, after the rescales its scores asked for (rare);
         // each value is multiplied in place, so that O keeps its registers.
         const int pb_i = (i - 1) & 1;
@@ -1482,17 +1496,11 @@ __global__ __launch_bounds__(kWsThreads, 1) void split_ws_kernel(Args a, int slo
                 vt[(c + 2) % 3][1] =
                     __builtin_amdgcn_ds_read_tr16_b64_v4bf16((bf16x4 LDS_AS*)(vptr(cb0 + c + 2) + 16 * kRowBytes));
             }
-            // the nine gathers of tile i+2, spread over the eight column blocks
-#pragma unroll
-            for (int j = c * kLoadsPerWave / kWsCols; j < (c + 1) * kLoadsPerWave / kWsCols; ++j)
-                gather16_slot(g_src(j, idx_n[j]), gdst, j);
             const bf16x8 va = __builtin_shufflevector(vt[c % 3][0], vt[c % 3][1], 0, 1, 2, 3, 4, 5, 6, 7);
 #pragma unroll
             for (int r = 0; r < kWaves; ++r)
                 o[r][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[r], o[r][c], 0, 0, 0);
         }
-        if (i + 3 < ntiles)
-            load_idx(i + 3, idx_n);
     }
     // this slice's O, rounded to bf16, in the register-fragment order of the
     // row blocks
@@ -1511,9 +1519,6 @@ __global__ __launch_bounds__(kWsThreads, 1) void split_ws_kernel(Args a, int slo
                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
     }
-    // The last gathers write LDS, so they land before the workgroup ends; the
-    // 32 stores are younger, and vmcnt retires in order.
-    wait_vmcnt<kColBlocks>();
 }
 
 // Merge of one (sequence b, 16-row block rb, group xblk of column units) by
