@@ -1108,13 +1108,12 @@ slice_done:
 
 // Split kernel with the work of one 64-row group divided between two kinds of
 // wave, two waves per SIMD (per-token table, one 16-row block per wave):
-// - score waves (0..3) hold Q for their 16 rows, stage the index windows and
-//   gather the rows of later tiles, read K from LDS, compute S^T = K.Q^T,
-//   mask, keep the running max and sum, and publish the bf16 weights P of a
-//   tile in LDS;
+// - score waves (0..3) hold Q for their 16 rows, stage the index windows,
+//   read K from LDS, compute S^T = K.Q^T, mask, keep the running max and sum,
+//   and publish the bf16 weights P of a tile in LDS;
 // - value waves (4..7) each hold O for all 64 rows and 128 of the 512
-//   columns and accumulate O^T += V^T.P^T one tile behind the score waves,
-//   with no global memory traffic until their final stores. Split by
+//   columns and accumulate O^T += V^T.P^T one tile behind the score waves.
+//   Split by
 //   columns, each value wave reads a quarter of the tile's V^T and the four
 //   row blocks' weights, and each V^T operand feeds four MFMAs: the tile's LDS
 //   reads of V fall to a quarter, and LDS bandwidth is what bounds the tile.
@@ -1124,17 +1123,46 @@ slice_done:
 // split_kernel<true, 1> (hybrid paging) in the same order, so a per-token call
 // and a paged call over the same rows give the same bits.
 //
-// Iteration i (0..ntiles) of both kinds starts at one barrier. Before it, the
-// score waves have waited for the gathers of tile i (only tile i+1's may still
-// be in flight) and published P(i-1). After it, the score waves work on tile i
-// (ring slot i % 4) and gather tile i+2 into slot (i+2) % 4, whose last
-// readers (tile i-2) finished before the barrier; the value waves work on
-// tile i-1 (slot (i-1) % 4). P and the rescale flag of tile i use buffer
-// i % 2, read by the value waves in iteration i+1.
+// Wave w of each kind gathers its share of tile rows 8w .. 8w+7: the score
+// wave five of the nine 1 KB loads, the value wave four (measured against all
+// nine on either kind: the tile is 1-2 % shorter, same bits).
+//
+// Iteration i (0..ntiles) of both kinds starts at one barrier. Before it, each
+// wave has waited for its gathers of tile i (only tile i+1's may still be in
+// flight) and the score waves have published P(i-1). After it, the score waves
+// work on tile i (ring slot i % 4), the value waves on tile i-1 (slot
+// (i-1) % 4), and both gather tile i+2 into slot (i+2) % 4, whose last readers
+// (tile i-2) finished before the barrier. P and the rescale flag of tile i use
+// buffer i % 2, read by the value waves in iteration i+1.
 constexpr int kWsThreads = 512;
 constexpr int kWsStages = 4;
 constexpr int kWsWinTiles = 16;                       // tiles per staged index window
 constexpr int kWsWinKeys = kWsWinTiles * kTileKeys;   // 512 page indices per window
+constexpr int kWsScoreLoads = 5;  // of a wave's nine row loads per tile; the value waves issue the rest
+
+// Gather plan of loads J0 .. J1-1 of a wave (wave w fills rows 8w .. 8w+7 of a
+// tile): load j puts lane l's 16 bytes at row kl = (64j + l) / 72, chunk
+// (64j + l) % 72 (stored at chunk ^ swz(kl)); gcs holds the byte offset less
+// 1024 (j % 4), as gather16_slot takes it.
+template <int J0, int J1>
+__device__ __forceinline__ void ws_plan(int lane, int* gcs, int* gkl)
+{
+#pragma unroll
+    for (int j = J0; j < J1; ++j) {
+        const int z = j * 64 + lane;
+        gkl[j] = z / kChunks;
+        gcs[j] = ((z - gkl[j] * kChunks) ^ swz(gkl[j])) * 16 - (j & 3) * 1024;
+    }
+}
+
+// Slots of loads J0 .. J1-1 from a tile's 8 staged page indices (clamped to the pool).
+template <int J0, int J1>
+__device__ __forceinline__ void ws_load_idx(const int* tidx, const int* gkl, int maxslot, int* out)
+{
+#pragma unroll
+    for (int j = J0; j < J1; ++j)
+        out[j] = clamp_slot(tidx[gkl[j]], maxslot);
+}
 
 __global__ __launch_bounds__(kWsThreads, 1) void split_ws_kernel(Args a, int slots, int single_c,
                                                                  int max_slices, int row_groups,
@@ -1250,6 +1278,9 @@ __global__ __launch_bounds__(kWsThreads, 1) void split_ws_kernel(Args a, int slo
     const int tree0 = S - N;
     const uint32_t lds0 = (uint32_t)(uintptr_t)(LDS_AS char*)s_kv;
     const uint64_t kv_addr = (uint64_t)(uintptr_t)a.kv;
+    auto slot_lds = [&](int t) {  // this wave's rows of ring slot t % 4
+        return lds0 + (uint32_t)((t % kWsStages) * kTileBytes + rw * (kKeysPerWave * kRowBytes));
+    };
 
     if (score) {
         // ------------------------------------------------ score waves
@@ -1278,40 +1309,29 @@ __global__ __launch_bounds__(kWsThreads, 1) void split_ws_kernel(Args a, int slo
         wait_vmcnt<0>();
         __syncthreads();  // index window 0 staged
 
-        // Gather plan: wave rw fills rows 8 rw .. 8 rw + 7 of each tile.
-        int gcs[kLoadsPerWave];
-        int gkl[kLoadsPerWave];
-#pragma unroll
-        for (int j = 0; j < kLoadsPerWave; ++j) {
-            const int z = j * 64 + lane;
-            gkl[j] = z / kChunks;
-            gcs[j] = ((z - gkl[j] * kChunks) ^ swz(gkl[j])) * 16 - (j & 3) * 1024;
-        }
-        auto g_src = [&](int j, int slot) { return kv_addr + (uint64_t)((int64_t)slot * kRowBytes + gcs[j]); };
-        auto load_idx = [&](int t, int* out) {
-            const int* tidx = &s_idx[(t / kWsWinTiles) & 1][(t % kWsWinTiles) * kTileKeys + rw * kKeysPerWave];
-#pragma unroll
-            for (int j = 0; j < kLoadsPerWave; ++j)
-                out[j] = clamp_slot(tidx[gkl[j]], maxslot);
-        };
-        auto slot_lds = [&](int t) {
-            return lds0 + (uint32_t)((t % kWsStages) * kTileBytes + rw * (kKeysPerWave * kRowBytes));
-        };
+        // This kind's row loads: 0 .. kWsScoreLoads-1 of the wave's nine.
         // Gathers go out for every iteration; past the last tile they repeat the
         // last staged indices into a free slot (rows already fetched, never
         // read), which keeps one wait count for every iteration.
-        int idx_n[kLoadsPerWave];
-        load_idx(0, idx_n);
+        constexpr int kJ1 = kWsScoreLoads;
+        int gcs[kLoadsPerWave], gkl[kLoadsPerWave], idx_n[kLoadsPerWave];
+        ws_plan<0, kJ1>(lane, gcs, gkl);
+        auto g_src = [&](int j, int slot) { return kv_addr + (uint64_t)((int64_t)slot * kRowBytes + gcs[j]); };
+        auto load_idx = [&](int t) {
+            ws_load_idx<0, kJ1>(&s_idx[(t / kWsWinTiles) & 1][(t % kWsWinTiles) * kTileKeys + rw * kKeysPerWave],
+                                gkl, maxslot, idx_n);
+        };
+        load_idx(0);
 #pragma unroll
-        for (int j = 0; j < kLoadsPerWave; ++j)
+        for (int j = 0; j < kJ1; ++j)
             gather16_slot(g_src(j, idx_n[j]), slot_lds(0), j);
         if (ntiles > 1)
-            load_idx(1, idx_n);
+            load_idx(1);
 #pragma unroll
-        for (int j = 0; j < kLoadsPerWave; ++j)
+        for (int j = 0; j < kJ1; ++j)
             gather16_slot(g_src(j, idx_n[j]), slot_lds(1), j);
         if (ntiles > 2)
-            load_idx(2, idx_n);
+            load_idx(2);
 
         const int fk = swz(rl);
         const int koff0 = rl * kRowBytes + 16 * (lg ^ fk);
@@ -1320,13 +1340,13 @@ __global__ __launch_bounds__(kWsThreads, 1) void split_ws_kernel(Args a, int slo
         float m_ref = -INFINITY, l_run = 0.f;
         constexpr int kKGroup = 4;
         constexpr int kKReads = 2 * kKSteps;
-        static_assert(kKReads / kKGroup == kLoadsPerWave, "one gather per K-operand group");
+        static_assert(kKReads / kKGroup >= kJ1, "at most one gather per K-operand group");
         int cur_off = 0;
         for (int i = 0; i <= ntiles; ++i) {
-            // tile i landed (only tile i+1's gathers may be in flight) and
-            // P(i-1) with its rescale flag and factors is written; the value
-            // waves are past P(i-2)
-            wait_vmcnt_lds<kLoadsPerWave>();
+            // this kind's rows of tile i landed (only tile i+1's gathers may
+            // be in flight) and P(i-1) with its rescale flag and factors is
+            // written; the value waves are past P(i-2)
+            wait_vmcnt_lds<kJ1>();
             __syncthreads();
             if (i == ntiles)
                 break;
@@ -1355,7 +1375,8 @@ __global__ __launch_bounds__(kWsThreads, 1) void split_ws_kernel(Args a, int slo
                         kf[(g + 1) & 1][j] = *(const bf16x8 LDS_AS*)kptr((g + 1) * kKGroup + j);
                 }
                 // gather g of tile i+2 (into the slot tile i-2 used)
-                gather16_slot(g_src(g, idx_n[g]), gdst, g);
+                if (g < kJ1)
+                    gather16_slot(g_src(g, idx_n[g]), gdst, g);
 #pragma unroll
                 for (int j = 0; j < kKGroup; ++j) {
                     const int n = g * kKGroup + j;
@@ -1420,7 +1441,7 @@ __global__ __launch_bounds__(kWsThreads, 1) void split_ws_kernel(Args a, int slo
             }
             s_p[pb_i][rw][lane] = pb;
             if (i + 3 < ntiles)
-                load_idx(i + 3, idx_n);
+                load_idx(i + 3);
             cur_off = cur_off == (kWsStages - 1) * kTileBytes ? 0 : cur_off + kTileBytes;
         }
         // this slice's (max, sum) per row; the last (repeated) gathers land
@@ -1439,6 +1460,28 @@ __global__ __launch_bounds__(kWsThreads, 1) void split_ws_kernel(Args a, int slo
 
     // ---------------------------------------------------- value waves
     __syncthreads();  // index window 0 staged
+    // This kind's row loads: kWsScoreLoads .. 8 of the wave's nine, two tiles
+    // ahead like the score waves' (and repeated past the last tile alike).
+    constexpr int kJ0 = kWsScoreLoads;
+    constexpr int kVLoads = kLoadsPerWave - kJ0;
+    int gcs[kLoadsPerWave], gkl[kLoadsPerWave], idx_n[kLoadsPerWave];
+    ws_plan<kJ0, kLoadsPerWave>(lane, gcs, gkl);
+    auto g_src = [&](int j, int slot) { return kv_addr + (uint64_t)((int64_t)slot * kRowBytes + gcs[j]); };
+    auto load_idx = [&](int t) {
+        ws_load_idx<kJ0, kLoadsPerWave>(
+            &s_idx[(t / kWsWinTiles) & 1][(t % kWsWinTiles) * kTileKeys + rw * kKeysPerWave], gkl, maxslot, idx_n);
+    };
+    load_idx(0);
+#pragma unroll
+    for (int j = kJ0; j < kLoadsPerWave; ++j)
+        gather16_slot(g_src(j, idx_n[j]), slot_lds(0), j);
+    if (ntiles > 1)
+        load_idx(1);
+#pragma unroll
+    for (int j = kJ0; j < kLoadsPerWave; ++j)
+        gather16_slot(g_src(j, idx_n[j]), slot_lds(1), j);
+    if (ntiles > 2)
+        load_idx(2);
     const int vkey = 4 * lg + (rl >> 2);
     const int fv = swz(vkey);
     const int vsel = (rl & 3) >> 1;
@@ -1456,9 +1499,19 @@ __global__ __launch_bounds__(kWsThreads, 1) void split_ws_kernel(Args a, int slo
         for (int c = 0; c < kWsCols; ++c)
             o[r][c] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    __syncthreads();  // iteration 0: the score waves work on tile 0
+    // iteration 0: the score waves work on tile 0; this kind gathers tile 2
+    wait_vmcnt<kVLoads>();
+    __syncthreads();
+#pragma unroll
+    for (int j = kJ0; j < kLoadsPerWave; ++j)
+        gather16_slot(g_src(j, idx_n[j]), slot_lds(2), j);
+    if (3 < ntiles)
+        load_idx(3);
     for (int i = 1; i <= ntiles; ++i) {
+        // this kind's rows of tile i landed (only tile i+1's may be in flight)
+        wait_vmcnt<kVLoads>();
         __syncthreads();  // P(i-1) published
+        const uint32_t gdst = slot_lds(i + 2);
         // P.V of tile i-1, after the rescales its scores asked for (rare);
         // each value is multiplied in place, so that O keeps its registers.
         const int pb_i = (i - 1) & 1;
@@ -1497,10 +1550,17 @@ __global__ __launch_bounds__(kWsThreads, 1) void split_ws_kernel(Args a, int slo
                     __builtin_amdgcn_ds_read_tr16_b64_v4bf16((bf16x4 LDS_AS*)(vptr(cb0 + c + 2) + 16 * kRowBytes));
             }
             const bf16x8 va = __builtin_shufflevector(vt[c % 3][0], vt[c % 3][1], 0, 1, 2, 3, 4, 5, 6, 7);
+            // this kind's gathers of tile i+2 (into the slot tile i-2 used),
+            // spread over the column blocks
+#pragma unroll
+            for (int j = kJ0 + c * kVLoads / kWsCols; j < kJ0 + (c + 1) * kVLoads / kWsCols; ++j)
+                gather16_slot(g_src(j, idx_n[j]), gdst, j);
 #pragma unroll
             for (int r = 0; r < kWaves; ++r)
                 o[r][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[r], o[r][c], 0, 0, 0);
         }
+        if (i + 3 < ntiles)
+            load_idx(i + 3);
     }
     // this slice's O, rounded to bf16, in the register-fragment order of the
     // row blocks
@@ -1519,6 +1579,9 @@ __global__ __launch_bounds__(kWsThreads, 1) void split_ws_kernel(Args a, int slo
                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
     }
+    // The last (repeated) gathers write LDS, so they land before the
+    // workgroup ends; the 32 stores are younger, and vmcnt retires in order.
+    wait_vmcnt<kWaves * kWsCols>();
 }
 
 // Merge of one (sequence b, 16-row block rb, group xblk of column units) by
