@@ -748,7 +748,7 @@ def roofline_entry(hd, achieved, prof):
     FETCH_SIZE/WRITE_SIZE counters saw per launch (traffic) and per call
     (call_traffic, against the call's algorithmic bytes), and the MFMA busy
     share."""
-    r = {"bound": "hbm", "kernel": "split_kernel",
+    r = {"bound": "hbm", "kernel": "split_ws_kernel",
          "achieved": round(achieved, 1), "peak": PEAK_GBPS, "unit": "GB/s",
          "frac": round(achieved / PEAK_GBPS, 4), "traffic": None,
          "avg_launch_us": round(hd["split_avg_ms"] * 1e3, 3),
@@ -756,7 +756,7 @@ def roofline_entry(hd, achieved, prof):
     if prof is None:
         r["profile"] = None
         return r
-    k = prof["kernels"]["split_kernel"]
+    k = prof["kernels"]["split_ws_kernel"]
     r["profile"] = os.path.relpath(PROFILE_FILE, ROOT)
     r["traffic"] = k.get("hbm_bytes_per_dispatch")
     if r["traffic"]:
